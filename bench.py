@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused 3x3 conv + epilogue kernels on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the fused op over the whole batch of the workload
+(inputs already resident in device memory).  The default workload is the
+16->64 conv on x [128,16,256,256] with the channel-min -> tanh -> tanh
+epilogue.  Prints ONE JSON line on stdout.
+
+Timing: W untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize() on both sides (wall clock -> ms_per_step).  HIP
+events recorded on the launch stream around the same K launches give the
+per-launch kernel duration used for the roofline figure.
+
+The CPU baseline is the oracle (test infrastructure) timed on a bounded
+batch slice of the same workload on the host cores; the GPU result for that
+slice is compared with it (max-abs error reported under "parity").
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused conv3x3+epilogue ms/iter & effective TFLOP/s (% fp32 MFMA peak)"
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak (AMD spec)
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E (AMD spec)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "x3_conv2d_epilogue_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE,
+    WRITE_SIZE), stored in profiles/traffic.json together with the hash of
+    the kernel sources they were taken on; None if absent or stale."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    e = d.get("workloads", {}).get(workload)
+    if not e or d.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return e
+
+
+def make_op(x3, wl, g, out=None, workspace=None):
+    p = wl.params
+    if wl.op == "min_tanh2":
+        return lambda: x3.conv3x3_min_tanh2(g["x"], g["weight"], g["bias"], out=out)
+    if wl.op == "scale_min":
+        return lambda: x3.conv3x3_scale_min(g["x"], g["weight"], g["bias"], p["scale"], out=out)
+    if wl.op == "mul_lrelu_gelu":
+        return lambda: x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"],
+                                                 p["neg_slope"], out=out)
+    if wl.op == "gn_scale_pool_clamp":
+        return lambda: x3.conv3x3_gn_scale_pool_clamp(
+            g["x"], g["weight"], g["bias"], g["gamma"], g["beta"], g["scale"], p["groups"],
+            p["eps"], p["pool_k"], p["lo"], p["hi"], out=out, workspace=workspace)
+    raise ValueError(wl.op)
+
+
+def out_shape(wl):
+    if wl.op in ("min_tanh2", "scale_min"):
+        return (wl.B, 1, wl.Ho, wl.Wo)
+    if wl.op == "mul_lrelu_gelu":
+        return (wl.B, wl.Cout, wl.Ho, wl.Wo)
+    k = wl.params["pool_k"]
+    return (wl.B, wl.Cout, (wl.Ho - k) // k + 1, (wl.Wo - k) // k + 1)
+
+
+def algorithmic_bytes(wl) -> int:
+    """x read once + weights + bias + per-channel params + output written."""
+    n_out = math.prod(out_shape(wl))
+    n_par = {"mul_lrelu_gelu": 1, "gn_scale_pool_clamp": 3}.get(wl.op, 0) * wl.Cout
+    return 4 * (wl.B * wl.Cin * wl.H * wl.W + wl.Cout * wl.Cin * 9 + wl.Cout + n_par + n_out)
+
+
+def time_op(torch, op, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        op()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        op()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
+def gpu_inputs(torch, wl, dev, seed=0, cpu_inputs=None):
+    """Device-resident inputs.  Given CPU inputs (the seeded generator), copy
+    them; otherwise draw the same distributions directly on the device."""
+    if cpu_inputs is not None:
+        return {k: v.to(dev) for k, v in cpu_inputs.items()}
+    g = torch.Generator(device=dev).manual_seed(seed)
+    a = 1.0 / math.sqrt(wl.Cin * 9)
+    d = {"x": torch.randn((wl.B, wl.Cin, wl.H, wl.W), generator=g, device=dev),
+         "weight": torch.empty((wl.Cout, wl.Cin, 3, 3), device=dev).uniform_(-a, a, generator=g),
+         "bias": torch.empty((wl.Cout,), device=dev).uniform_(-a, a, generator=g)}
+    if wl.op == "mul_lrelu_gelu":
+        d["multiplier"] = 1 + 0.1 * torch.randn((wl.Cout,), generator=g, device=dev)
+    if wl.op == "gn_scale_pool_clamp":
+        d["gamma"] = 1 + 0.1 * torch.randn((wl.Cout,), generator=g, device=dev)
+        d["beta"] = 0.1 * torch.randn((wl.Cout,), generator=g, device=dev)
+        d["scale"] = 1 + 0.1 * torch.randn((wl.Cout,), generator=g, device=dev)
+    return d
+
+
+def cpu_baseline(wl, cpu_in, gpu_out, budget_s):
+    """Time the oracle on a contiguous batch slice [0, b) of the workload,
+    b chosen so the run takes about `budget_s` seconds; compare the GPU
+    output on that slice."""
+    import numpy as np
+    import oracle
+
+    def run(b):
+        x = cpu_in["x"][:b].numpy()
+        w, bias = cpu_in["weight"].numpy(), cpu_in["bias"].numpy()
+        p = wl.params
+        if wl.op == "min_tanh2":
+            return oracle.min_tanh2(x, w, bias)
+        if wl.op == "scale_min":
+            return oracle.scale_min(x, w, bias, p["scale"])
+        if wl.op == "mul_lrelu_gelu":
+            return oracle.mul_lrelu_gelu(x, w, bias, cpu_in["multiplier"].numpy(), p["neg_slope"])
+        return oracle.gn_scale_pool_clamp(x, w, bias, cpu_in["gamma"].numpy(),
+                                          cpu_in["beta"].numpy(), cpu_in["scale"].numpy(),
+                                          p["groups"], p["eps"], p["pool_k"], p["lo"], p["hi"])
+
+    t0 = time.perf_counter()
+    ref = run(1)
+    t1 = time.perf_counter() - t0
+    b = max(1, min(wl.B, int(budget_s / max(t1, 1e-3))))
+    if b > 1:
+        t0 = time.perf_counter()
+        ref = run(b)
+        dt = time.perf_counter() - t0
+    else:
+        dt = t1
+    sub = wl.with_batch(b)
+    got = gpu_out[:b].detach().cpu().numpy().astype(np.float64)
+    err = float(np.abs(got - ref).max())
+    return {
+        "value": round(sub.conv_flops() / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"batch slice [0,{b}) of {wl.B} ({b * wl.Cin * wl.H * wl.W} input values), "
+                  f"{dt:.2f} s wall; the full workload would take ~{dt * wl.B / b:.0f} s",
+        "seconds": round(dt, 3),
+    }, {"max_abs_err": err, "samples": b, "tolerance": 2e-4, "ok": err <= 2e-4}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="min_tanh2")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="do not time the other four workloads")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
+              "the multi-GPU path is design-only (batch sharding, no collectives).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import x3_conv2d_epilogue_amd as x3
+    from x3_conv2d_epilogue_amd.synthetic import WORKLOAD_ORDER, WORKLOADS, make_inputs
+
+    x3.load_library()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+
+    log(f"generating {wl.about} (seed 0, CPU)")
+    cpu_in = make_inputs(wl, seed=0)
+    g = gpu_inputs(torch, wl, dev, cpu_inputs=cpu_in)
+    out = torch.empty(out_shape(wl), device=dev)
+    ws = None
+    if wl.op == "gn_scale_pool_clamp":
+        p = wl.params
+        ws = torch.empty(x3.gn_workspace_bytes(wl.B, wl.Cin, wl.H, wl.W, wl.Cout, p["groups"],
+                                               p["pool_k"]), dtype=torch.uint8, device=dev)
+    op = make_op(x3, wl, g, out=out, workspace=ws)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written x3")
+
+    log(f"timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    ms_wall, ms_kernel = time_op(torch, op, args.steps, args.warmup)
+    flops = wl.conv_flops()
+    tflops = flops / (ms_wall * 1e-3) / 1e12
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+
+    traffic = load_traffic(args.workload)
+    roof = {
+        "bound": "mfma",
+        "achieved": round(achieved, 3),
+        "peak": PEAK_FP32_MFMA_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+        "traffic": traffic["bytes_per_launch"] if traffic else None,
+        "kernel_ms": round(ms_kernel, 4),
+        "algorithmic_flop_per_launch": flops,
+        "algorithmic_bytes_per_launch": algorithmic_bytes(wl),
+    }
+    if wl.op == "gn_scale_pool_clamp":
+        roof["note"] = "two kernels per launch (conv pass + finalize); kernel_ms covers both"
+
+    others = {}
+    if not args.no_others:
+        for name in WORKLOAD_ORDER:
+            if name == args.workload:
+                continue
+            w2 = WORKLOADS[name]
+            g2 = gpu_inputs(torch, w2, dev, seed=0)
+            o2 = torch.empty(out_shape(w2), device=dev)
+            ws2 = None
+            if w2.op == "gn_scale_pool_clamp":
+                q = w2.params
+                ws2 = torch.empty(x3.gn_workspace_bytes(w2.B, w2.Cin, w2.H, w2.W, w2.Cout,
+                                                        q["groups"], q["pool_k"]),
+                                  dtype=torch.uint8, device=dev)
+            op2 = make_op(x3, w2, g2, out=o2, workspace=ws2)
+            steps2 = max(3, min(args.steps, 20))
+            mw, mk = time_op(torch, op2, steps2, max(1, args.warmup))
+            f2 = w2.conv_flops()
+            others[name] = {
+                "about": w2.about, "ms_per_step": round(mw, 4), "kernel_ms": round(mk, 4),
+                "tflops": round(f2 / (mk * 1e-3) / 1e12, 3),
+                "frac_fp32_mfma_peak": round(f2 / (mk * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+                "steps": steps2,
+            }
+            del g2, o2, ws2, op2
+            torch.cuda.empty_cache()
+
+    cpu = None
+    parity = None
+    if args.cpu_budget > 0:
+        op()
+        torch.cuda.synchronize()
+        log(f"cpu baseline: oracle on the host cores (~{args.cpu_budget:.0f} s)")
+        cpu, parity = cpu_baseline(wl, cpu_in, out, args.cpu_budget)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded: x~N(0,1), w,b~U(+-1/sqrt(Cin*9)))",
+        "config": {"workload": wl.about, "x_shape": [wl.B, wl.Cin, wl.H, wl.W],
+                   "cout": wl.Cout, "out_shape": list(out_shape(wl)), "seed": 0,
+                   "flop_per_step": flops},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "other_workloads": others,
+        "host": {"cpu": platform.processor() or platform.machine(), "cpu_count": os.cpu_count(),
+                 "device": torch.cuda.get_device_name(0)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+/*
+ * x3conv.h -- C ABI of the fused 3x3 convolution + epilogue library for
+ * AMD Instinct MI355X (gfx950).  Library: libx3conv.so.
+ *
+ * Every compute entry point runs one valid 3x3 convolution with bias
+ * (stride 1, no padding, dilation 1, groups 1) as an implicit GEMM on the
+ * fp32 matrix cores, and applies its epilogue while the convolution result
+ * is still in registers, so the full convolution output is never written to
+ * device memory.
+ *
+ * Sources, cited by page and passage (the pages have no numbered sections):
+ *   [P25] POPCORNBENCH level-2 problem 25 transcript (Kimi-K2.6): Conv2d
+ *         16->64 k3, torch.min over channels with keepdim, tanh, tanh.
+ *   [P54] POPCORNBENCH level-2 problem 54 transcript: Conv2d 64->64 k3,
+ *         per-channel multiplier [C,1,1], LeakyReLU, GELU (exact erf form).
+ *   [P32] POPCORNBENCH level-2 problem 32 transcript: Conv2d 64->128 k3,
+ *         multiply by 2.0, min over channels with keepdim; its opening
+ *         analysis derives the valid output size H-2.
+ *   [P85] POPCORNBENCH level-2 problem 85 transcript: Conv2d 8->64 k3,
+ *         GroupNorm(16 groups, eps 1e-5, affine), per-channel scale [C,1,1],
+ *         MaxPool2d(4) (stride 4, floor mode), clamp(0, 1).
+ *
+ * Common conventions
+ * ------------------
+ * - Every tensor pointer is a DEVICE pointer to contiguous fp32 data that
+ *   the caller allocated and owns; the library never allocates, frees or
+ *   synchronizes.
+ *     x    [B][Cin][H][W]        NCHW
+ *     w    [Cout][Cin][3][3]
+ *     b    [Cout]
+ *   The convolution output y has shape [B][Cout][Ho][Wo], Ho = H-2,
+ *   Wo = W-2 ([P32], opening analysis of the reference model):
+ *     y[n,co,h,w] = b[co] + sum_{ci,kh,kw} x[n,ci,h+kh,w+kw] * w[co,ci,kh,kw]
+ * - `stream` is a hipStream_t (0 = the null stream).  Work is enqueued on it
+ *   and the call returns at once; device-side faults surface at the caller's
+ *   next synchronization.
+ * - Arguments are validated before anything is enqueued.  No call aborts or
+ *   prints; the return value is an x3_status and x3_last_error() gives a
+ *   thread-local detail string for the last failure on the calling thread.
+ * - `out` must not overlap any input.  Inputs are never written.
+ * - Supported: Cout in {64, 128}; 3 <= H, W; Cin >= 1; each sample of x
+ *   smaller than 2 GiB; every other positive shape works (ragged tiles are
+ *   masked inside the kernels).  Anything else returns X3_EUNSUPPORTED.
+ * - B == 0 is a valid empty call: nothing is enqueued and X3_OK is returned.
+ */
+#ifndef X3CONV_H
+#define X3CONV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int x3_status;
+enum {
+  X3_OK = 0,            /* enqueued (or nothing to do) */
+  X3_EINVAL = 1,        /* null pointer, negative size, non-finite scalar */
+  X3_ESHAPE = 2,        /* shape cannot produce an output (H or W < 3, ...) */
+  X3_EUNSUPPORTED = 3,  /* valid but not compiled in (e.g. Cout not 64/128) */
+  X3_EWORKSPACE = 4,    /* workspace missing or too small */
+  X3_EHIP = 5           /* the HIP runtime reported an error at launch */
+};
+
+/* Epilogue (a), [P25]: out[n,0,h,w] = tanh(tanh(min_co y[n,co,h,w])).
+ * out: [B][1][Ho][Wo]. */
+x3_status x3_conv3x3_min_tanh2_f32(const float* x, const float* w,
+                                   const float* b, float* out, int B, int Cin,
+                                   int H, int W, int Cout, void* stream);
+
+/* Epilogue (b), [P54]: v = y[n,co,h,w] * mult[co];
+ * v = (v >= 0) ? v : neg_slope * v  (LeakyReLU; the page uses 0.01);
+ * out[n,co,h,w] = 0.5 * v * (1 + erf(v / sqrt(2)))  (exact GELU).
+ * mult: [Cout] (the page's [Cout,1,1] parameter).  out: [B][Cout][Ho][Wo].
+ * neg_slope must be finite (else X3_EINVAL). */
+x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
+                                        const float* b, const float* mult,
+                                        float neg_slope, float* out, int B,
+                                        int Cin, int H, int W, int Cout,
+                                        void* stream);
+
+/* Epilogue (c), [P32]: out[n,0,h,w] = min_co (scale * y[n,co,h,w]).
+ * The page uses scale = 2.0; any finite scale is accepted (for scale < 0 the
+ * minimum of the scaled values is scale times the channel maximum).
+ * out: [B][1][Ho][Wo].  scale must be finite (else X3_EINVAL). */
+x3_status x3_conv3x3_scale_min_f32(const float* x, const float* w,
+                                   const float* b, float scale, float* out,
+                                   int B, int Cin, int H, int W, int Cout,
+                                   void* stream);
+
+/* Bytes of device workspace x3_conv3x3_gn_scale_pool_clamp_f32 needs for
+ * this shape (partial GroupNorm statistics).  Returns 0 when the shape is
+ * invalid or unsupported (the compute call then reports why). */
+size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W, int Cout,
+                                     int groups, int pool_k);
+
+/* Epilogue (d), [P85]: z = GroupNorm(y; groups, eps, gamma, beta)
+ * (per sample and group of Cout/groups consecutive channels: mean and
+ * biased variance over those channels and all Ho x Wo positions,
+ * (y - mean) / sqrt(var + eps) * gamma[c] + beta[c]); then z * scale[c];
+ * then MaxPool2d(pool_k, stride pool_k, no padding, floor mode); then
+ * clamp to [lo, hi] as min(max(., lo), hi).
+ * gamma, beta, scale: [Cout].  out: [B][Cout][Ph][Pw] with
+ * Ph = (Ho - pool_k) / pool_k + 1, Pw = (Wo - pool_k) / pool_k + 1.
+ * workspace: device memory of at least x3_conv3x3_gn_workspace_bytes(...)
+ * bytes, owned by the caller, contents need not be initialized; it is
+ * overwritten, and two calls sharing one workspace must be ordered on one
+ * stream.  Two kernels are enqueued on `stream` (statistics + window
+ * extrema, then finalize); `out` holds intermediate values between them.
+ * Supported: Cout / groups == 4, pool_k == 4 (else X3_EUNSUPPORTED);
+ * eps > 0 and finite lo <= hi (else X3_EINVAL); Ho, Wo >= pool_k (else
+ * X3_ESHAPE). */
+x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
+    const float* x, const float* w, const float* b, const float* gamma,
+    const float* beta, const float* scale, int groups, float eps, int pool_k,
+    float lo, float hi, float* out, void* workspace, size_t workspace_bytes,
+    int B, int Cin, int H, int W, int Cout, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* x3_status_str(x3_status s);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* x3_last_error(void);
+/* Library version string. */
+const char* x3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* X3CONV_H */

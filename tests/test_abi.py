@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/x3conv.h, and rejects invalid arguments with the
+documented status before enqueuing anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import x3_conv2d_epilogue_amd as x3
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "x3conv.h")
+
+OK, EINVAL, ESHAPE, EUNSUP, EWS, EHIP = range(6)
+P = ctypes.c_void_p
+
+
+def fake(addr):
+    """A non-null pointer value that validation accepts but never follows."""
+    return P(addr)
+
+
+X, W_, B_, O, M = fake(0x10000000), fake(0x20000000), fake(0x30000000), fake(0x40000000), \
+    fake(0x50000000)
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(x3_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return x3.load_library()
+
+
+def test_header_declares_expected_api():
+    assert header_functions() == sorted(x3.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", x3.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (x3_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    # nothing else leaks out of the library under the x3_ prefix
+    assert exported == set(header_functions())
+
+
+def test_status_strings_and_version(lib):
+    for s in range(6):
+        assert lib.x3_status_str(s)
+    assert lib.x3_status_str(99) == b"unknown status"
+    assert b"gfx950" in lib.x3_version()
+    assert x3.version().startswith("x3conv")
+
+
+def _min(lib, *args):
+    return lib.x3_conv3x3_min_tanh2_f32(*args)
+
+
+def test_min_tanh2_validation(lib):
+    s = P(0)
+    assert _min(lib, X, W_, B_, O, -1, 16, 32, 32, 64, s) == EINVAL
+    assert b"positive" in lib.x3_last_error()
+    assert _min(lib, X, W_, B_, O, 2, 0, 32, 32, 64, s) == EINVAL
+    assert _min(lib, X, W_, B_, O, 2, 16, 2, 32, 64, s) == ESHAPE
+    assert _min(lib, X, W_, B_, O, 2, 16, 32, 2, 64, s) == ESHAPE
+    assert _min(lib, X, W_, B_, O, 2, 16, 32, 32, 48, s) == EUNSUP
+    assert b"Cout=48" in lib.x3_last_error()
+    assert _min(lib, None, W_, B_, O, 2, 16, 32, 32, 64, s) == EINVAL
+    assert _min(lib, X, None, B_, O, 2, 16, 32, 32, 64, s) == EINVAL
+    assert _min(lib, X, W_, None, O, 2, 16, 32, 32, 64, s) == EINVAL
+    assert _min(lib, X, W_, B_, None, 2, 16, 32, 32, 64, s) == EINVAL
+    # out aliasing x
+    assert _min(lib, X, W_, B_, X, 2, 16, 32, 32, 64, s) == EINVAL
+    assert b"overlaps" in lib.x3_last_error()
+    # a sample of x of 2 GiB or more
+    assert _min(lib, X, W_, B_, O, 1, 8192, 256, 256, 64, s) == EUNSUP
+    # empty batch: valid, nothing enqueued (null x/out allowed)
+    assert _min(lib, None, W_, B_, None, 0, 16, 32, 32, 64, s) == OK
+
+
+def test_mul_lrelu_gelu_validation(lib):
+    f = lib.x3_conv3x3_mul_lrelu_gelu_f32
+    s = P(0)
+    assert f(X, W_, B_, None, 0.01, O, 2, 16, 32, 32, 64, s) == EINVAL
+    assert f(X, W_, B_, M, float("nan"), O, 2, 16, 32, 32, 64, s) == EINVAL
+    assert f(X, W_, B_, M, float("inf"), O, 2, 16, 32, 32, 64, s) == EINVAL
+    assert f(X, W_, B_, M, 0.01, O, 2, 16, 32, 32, 96, s) == EUNSUP
+    assert f(X, W_, B_, M, 0.01, M, 2, 16, 32, 32, 64, s) == EINVAL  # out == mult
+    assert f(None, W_, B_, M, 0.01, None, 0, 16, 32, 32, 64, s) == OK
+
+
+def test_scale_min_validation(lib):
+    f = lib.x3_conv3x3_scale_min_f32
+    s = P(0)
+    assert f(X, W_, B_, float("nan"), O, 2, 64, 32, 32, 128, s) == EINVAL
+    assert f(X, W_, B_, 2.0, O, 2, 64, 1, 32, 128, s) == ESHAPE
+    assert f(X, W_, B_, 2.0, O, 2, 64, 32, 32, 256, s) == EUNSUP
+    assert f(X, W_, B_, 2.0, B_, 2, 64, 32, 32, 128, s) == EINVAL  # out == bias
+
+
+def test_gn_workspace_bytes(lib):
+    f = lib.x3_conv3x3_gn_workspace_bytes
+    # [128,8,128,128] -> conv 126x126, tiles of 8 rows x 128 columns, 8 waves:
+    # 16 row tiles * 1 column tile * 8 = 128 partial slots per (n, g) of 16 B
+    assert f(128, 8, 128, 128, 64, 16, 4) == 128 * 16 * 128 * 16
+    assert f(0, 8, 128, 128, 64, 16, 4) == 0
+    assert f(2, 8, 128, 128, 64, 15, 4) == 0   # 64 % 15
+    assert f(2, 8, 128, 128, 64, 8, 4) == 0    # 8 channels per group: not compiled
+    assert f(2, 8, 128, 128, 64, 16, 3) == 0   # pool 3: not compiled
+    assert f(2, 8, 5, 5, 64, 16, 4) == 0       # 3x3 conv output < pool window
+    assert f(2, 8, 128, 128, 128, 32, 4) == 0  # Cout 128: not compiled for GN
+
+
+def test_gn_validation(lib):
+    f = lib.x3_conv3x3_gn_scale_pool_clamp_f32
+    s = P(0)
+    ws = fake(0x60000000)
+    need = lib.x3_conv3x3_gn_workspace_bytes(2, 8, 34, 34, 64, 16, 4)
+    assert need > 0
+
+    def call(**kw):
+        a = dict(x=X, w=W_, b=B_, g=M, be=fake(0x51000000), sc=fake(0x52000000), groups=16,
+                 eps=1e-5, k=4, lo=0.0, hi=1.0, out=O, ws=ws, wsb=need, B=2, Cin=8, H=34, W=34,
+                 Cout=64)
+        a.update(kw)
+        return f(a["x"], a["w"], a["b"], a["g"], a["be"], a["sc"], a["groups"], a["eps"], a["k"],
+                 a["lo"], a["hi"], a["out"], a["ws"], a["wsb"], a["B"], a["Cin"], a["H"], a["W"],
+                 a["Cout"], s)
+
+    assert call(groups=0) == EINVAL
+    assert call(k=0) == EINVAL
+    assert call(groups=5) == ESHAPE
+    assert call(H=5) == ESHAPE
+    assert call(groups=8) == EUNSUP
+    assert call(k=2) == EUNSUP
+    assert call(Cout=128, groups=32) == EUNSUP
+    assert call(eps=0.0) == EINVAL
+    assert call(eps=float("nan")) == EINVAL
+    assert call(lo=1.0, hi=0.0) == EINVAL
+    assert call(hi=float("inf")) == EINVAL
+    assert call(g=None) == EINVAL
+    assert call(ws=None) == EWS
+    assert call(wsb=need - 1) == EWS
+    assert b"workspace" in lib.x3_last_error()
+    assert call(ws=fake(0x60000004)) == EINVAL  # misaligned workspace
+    assert call(out=X) == EINVAL
+    assert call(ws=O) == EINVAL  # workspace overlaps out
+    assert call(B=0, x=None, out=None) == OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 16, 8, 8)
+    w = torch.zeros(64, 16, 3, 3)
+    b = torch.zeros(64)
+    with pytest.raises(ValueError):
+        x3.conv3x3_min_tanh2(x, w, b)
+    with pytest.raises(TypeError):
+        x3.conv3x3_scale_min(x.double(), w, b)

@@ -1,0 +1,349 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Bar: max-abs error <= 2e-4 on fp32 outputs; bit-exact where the inputs make
+fp32 arithmetic exact (small integers: every partial sum is an integer below
+2^24, and scale 2.0 is exact).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import x3_conv2d_epilogue_amd as x3
+from x3_conv2d_epilogue_amd.synthetic import WORKLOADS, make_inputs, random_case
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(d):
+    return {k: v.to(DEV) for k, v in d.items()}
+
+
+def run_op(op, d, **kw):
+    g = to_dev(d)
+    if op == "min_tanh2":
+        out = x3.conv3x3_min_tanh2(g["x"], g["weight"], g["bias"])
+    elif op == "scale_min":
+        out = x3.conv3x3_scale_min(g["x"], g["weight"], g["bias"], kw.get("scale", 2.0))
+    elif op == "mul_lrelu_gelu":
+        out = x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"],
+                                        kw.get("neg_slope", 0.01))
+    elif op == "gn_scale_pool_clamp":
+        out = x3.conv3x3_gn_scale_pool_clamp(
+            g["x"], g["weight"], g["bias"], g["gamma"], g["beta"], g["scale"],
+            kw.get("groups", 16), kw.get("eps", 1e-5), kw.get("pool_k", 4),
+            kw.get("lo", 0.0), kw.get("hi", 1.0))
+    else:
+        raise ValueError(op)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def run_oracle(op, d, **kw):
+    n = {k: v.numpy() for k, v in d.items()}
+    if op == "min_tanh2":
+        return oracle.min_tanh2(n["x"], n["weight"], n["bias"])
+    if op == "scale_min":
+        return oracle.scale_min(n["x"], n["weight"], n["bias"], kw.get("scale", 2.0))
+    if op == "mul_lrelu_gelu":
+        return oracle.mul_lrelu_gelu(n["x"], n["weight"], n["bias"], n["multiplier"],
+                                     kw.get("neg_slope", 0.01))
+    return oracle.gn_scale_pool_clamp(n["x"], n["weight"], n["bias"], n["gamma"], n["beta"],
+                                      n["scale"], kw.get("groups", 16), kw.get("eps", 1e-5),
+                                      kw.get("pool_k", 4), kw.get("lo", 0.0), kw.get("hi", 1.0))
+
+
+def assert_close(got, ref, tol=TOL, what=""):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    err = np.abs(got.astype(np.float64) - ref)
+    i = np.unravel_index(int(np.argmax(err)), err.shape) if err.size else None
+    mx = float(err.max()) if err.size else 0.0
+    say(f"  {what}: max_abs_err={mx:.3e} at {i}")
+    assert np.all(np.isfinite(got)), what
+    assert mx <= tol, f"{what}: max-abs {mx:.3e} > {tol} at {i}: got {got[i]} ref {ref[i]}"
+
+
+# Shapes that exercise every tile configuration (output width picks the
+# column-tile width), ragged rows and columns, several tiles per sample,
+# and Cin not a multiple of the 8-channel K chunk.
+SHAPES64 = [  # (B, Cin, H, W)
+    (2, 16, 32, 32),     # Wo=30: 1 strip, single ragged tile
+    (1, 3, 35, 35),      # Wo=33: 2 strips, 1 valid column in the 2nd
+    (2, 8, 41, 66),      # Wo=64: exactly 2 strips
+    (1, 12, 20, 67),     # Wo=65: 4-strip tiles, ragged
+    (2, 9, 13, 130),     # Wo=128
+    (1, 16, 11, 131),    # Wo=129: 8-strip tile
+    (1, 5, 9, 258),      # Wo=256
+    (1, 20, 7, 300),     # Wo=298: two column tiles, ragged
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES64)
+@pytest.mark.parametrize("Cout", [64, 128])
+def test_scale_min_integer_bit_exact(shape, Cout):
+    B, Cin, H, W = shape
+    say(f"scale_min int-exact {shape} Cout={Cout}")
+    d = random_case("scale_min", B, Cin, H, W, Cout, seed=100 + Cin, dist="int")
+    got = run_op("scale_min", d, scale=2.0)
+    ref = run_oracle("scale_min", d, scale=2.0)
+    assert np.array_equal(got.astype(np.float64), ref), \
+        f"max diff {np.abs(got - ref).max()}"
+
+
+@pytest.mark.parametrize("shape", SHAPES64[::2])
+def test_scale_min_negative_scale_integer_bit_exact(shape):
+    B, Cin, H, W = shape
+    d = random_case("scale_min", B, Cin, H, W, 64, seed=7, dist="int")
+    got = run_op("scale_min", d, scale=-1.0)
+    ref = run_oracle("scale_min", d, scale=-1.0)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("shape", SHAPES64)
+@pytest.mark.parametrize("Cout", [64, 128])
+def test_min_tanh2_random(shape, Cout):
+    B, Cin, H, W = shape
+    say(f"min_tanh2 {shape} Cout={Cout}")
+    d = random_case("min_tanh2", B, Cin, H, W, Cout, seed=200 + W)
+    assert_close(run_op("min_tanh2", d), run_oracle("min_tanh2", d), what=f"{shape}/{Cout}")
+
+
+@pytest.mark.parametrize("shape", SHAPES64)
+@pytest.mark.parametrize("Cout", [64, 128])
+def test_mul_lrelu_gelu_random(shape, Cout):
+    B, Cin, H, W = shape
+    say(f"mul_lrelu_gelu {shape} Cout={Cout}")
+    d = random_case("mul_lrelu_gelu", B, Cin, H, W, Cout, seed=300 + H)
+    assert_close(run_op("mul_lrelu_gelu", d), run_oracle("mul_lrelu_gelu", d),
+                 what=f"{shape}/{Cout}")
+
+
+@pytest.mark.parametrize("scale", [2.0, 0.37, -1.5])
+def test_scale_min_random_scales(scale):
+    d = random_case("scale_min", 2, 24, 19, 70, 128, seed=400)
+    assert_close(run_op("scale_min", d, scale=scale), run_oracle("scale_min", d, scale=scale),
+                 what=f"scale={scale}")
+
+
+def test_mul_lrelu_gelu_other_slope():
+    d = random_case("mul_lrelu_gelu", 1, 8, 14, 40, 64, seed=401)
+    assert_close(run_op("mul_lrelu_gelu", d, neg_slope=0.2),
+                 run_oracle("mul_lrelu_gelu", d, neg_slope=0.2), what="slope 0.2")
+
+
+GN_SHAPES = [  # (B, Cin, H, W)
+    (2, 8, 34, 34),     # Wo=32: 1 strip; 8 pooled columns
+    (1, 8, 22, 39),     # Wo=37: ragged strips, pooled 5x9
+    (2, 3, 40, 70),     # Wo=68
+    (1, 16, 18, 131),   # Wo=129
+    (1, 8, 14, 258),    # Wo=256, two row tiles
+    (1, 4, 11, 301),    # Wo=299: two column tiles
+]
+
+
+@pytest.mark.parametrize("shape", GN_SHAPES)
+@pytest.mark.parametrize("lohi", [(0.0, 1.0), (-100.0, 100.0)])
+def test_gn_pool_random(shape, lohi):
+    B, Cin, H, W = shape
+    say(f"gn_pool {shape} clamp={lohi}")
+    d = random_case("gn_scale_pool_clamp", B, Cin, H, W, 64, seed=500 + W)
+    kw = dict(groups=16, eps=1e-5, pool_k=4, lo=lohi[0], hi=lohi[1])
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw), run_oracle("gn_scale_pool_clamp", d, **kw),
+                 what=f"{shape}/{lohi}")
+
+
+def test_gn_pool_negative_gamma_and_scale():
+    d = random_case("gn_scale_pool_clamp", 2, 8, 30, 46, 64, seed=600)
+    d["gamma"][::3] *= -1.0
+    d["scale"][1::4] *= -1.0
+    d["scale"][5] = 0.0
+    kw = dict(lo=-50.0, hi=50.0)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw), run_oracle("gn_scale_pool_clamp", d, **kw),
+                 what="mixed signs")
+
+
+def test_gn_pool_all_ones_closed_form():
+    """x == 1, w == 1: per-channel constant conv; the result is
+    ((b[c]-mu_g)/sqrt(var_g+eps)*gamma[c]+beta[c])*scale[c], clamped."""
+    d = random_case("gn_scale_pool_clamp", 1, 8, 20, 20, 64, seed=601)
+    d["x"] = torch.ones_like(d["x"])
+    d["weight"] = torch.ones_like(d["weight"])
+    # dyadic biases (multiples of 1/64): 72 + b and the group sums are exact
+    # in fp32, so the GPU's statistics carry no rounding.  (With arbitrary
+    # biases a group's spread is ~0.03 against a mean of ~72, and the fp32
+    # rounding of 72 + b alone is amplified ~30x by the normalization.)
+    g = torch.Generator().manual_seed(602)
+    d["bias"] = torch.randint(-16, 17, (64,), generator=g).float() / 64.0
+    kw = dict(lo=-100.0, hi=100.0)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw), run_oracle("gn_scale_pool_clamp", d, **kw),
+                 what="all ones")
+
+
+def test_edge_minimal_spatial():
+    """H = W = 3: a single output pixel per sample."""
+    d = random_case("min_tanh2", 3, 7, 3, 3, 64, seed=700)
+    assert_close(run_op("min_tanh2", d), run_oracle("min_tanh2", d), what="3x3")
+    d = random_case("mul_lrelu_gelu", 2, 1, 3, 3, 128, seed=701)
+    assert_close(run_op("mul_lrelu_gelu", d), run_oracle("mul_lrelu_gelu", d), what="3x3 b")
+
+
+def test_edge_many_chunks():
+    d = random_case("scale_min", 1, 77, 12, 40, 128, seed=702)
+    assert_close(run_op("scale_min", d), run_oracle("scale_min", d), what="Cin=77")
+
+
+def test_edge_empty_batch():
+    d = to_dev(random_case("min_tanh2", 1, 4, 8, 8, 64, seed=703))
+    x0 = d["x"][:0]
+    out = x3.conv3x3_min_tanh2(x0, d["weight"], d["bias"])
+    assert tuple(out.shape) == (0, 1, 6, 6)
+
+
+def test_unsupported_cout_raises():
+    d = to_dev(random_case("min_tanh2", 1, 4, 8, 8, 32, seed=704))
+    with pytest.raises(x3.X3Error) as e:
+        x3.conv3x3_min_tanh2(d["x"], d["weight"], d["bias"])
+    assert e.value.status_name == "X3_EUNSUPPORTED"
+
+
+def test_non_default_stream_and_determinism():
+    d = random_case("mul_lrelu_gelu", 2, 16, 30, 70, 64, seed=800)
+    g = to_dev(d)
+    ref = x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"])
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out2 = x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"])
+    s.synchronize()
+    assert torch.equal(ref, out2)
+    gn = random_case("gn_scale_pool_clamp", 2, 8, 40, 40, 64, seed=801)
+    gg = to_dev(gn)
+    a1 = x3.conv3x3_gn_scale_pool_clamp(gg["x"], gg["weight"], gg["bias"], gg["gamma"],
+                                        gg["beta"], gg["scale"], lo=-9.0, hi=9.0)
+    a2 = x3.conv3x3_gn_scale_pool_clamp(gg["x"], gg["weight"], gg["bias"], gg["gamma"],
+                                        gg["beta"], gg["scale"], lo=-9.0, hi=9.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2)
+
+
+def test_guard_bands_untouched():
+    """Outputs written into the middle of a larger buffer leave the guard
+    bands on both sides intact."""
+    d = random_case("mul_lrelu_gelu", 1, 8, 17, 45, 64, seed=900)
+    g = to_dev(d)
+    n = 1 * 64 * 15 * 43
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 12345.0, device=DEV)
+    out = buf[pad:pad + n].view(1, 64, 15, 43)
+    x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"], out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[pad + n:] == 12345.0)
+    assert_close(out.cpu().numpy(), run_oracle("mul_lrelu_gelu", d), what="guarded")
+    # GroupNorm path: out and workspace both guarded
+    dg = random_case("gn_scale_pool_clamp", 1, 8, 30, 30, 64, seed=901)
+    gg = to_dev(dg)
+    need = x3.gn_workspace_bytes(1, 8, 30, 30, 64, 16, 4)
+    wbuf = torch.full((need // 4 + 2 * pad,), 777.0, device=DEV)
+    ws = wbuf[pad:pad + need // 4]
+    m = 64 * 7 * 7  # conv 28x28 -> (28 - 4) // 4 + 1 = 7 windows per axis
+    obuf = torch.full((m + 2 * pad,), 555.0, device=DEV)
+    o = obuf[pad:pad + m].view(1, 64, 7, 7)
+    x3.conv3x3_gn_scale_pool_clamp(gg["x"], gg["weight"], gg["bias"], gg["gamma"], gg["beta"],
+                                   gg["scale"], out=o, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(wbuf[:pad] == 777.0) and torch.all(wbuf[pad + need // 4:] == 777.0)
+    assert torch.all(obuf[:pad] == 555.0) and torch.all(obuf[pad + m:] == 555.0)
+    assert_close(o.cpu().numpy(), run_oracle("gn_scale_pool_clamp", dg), what="gn guarded")
+
+
+# ----------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the benchmark
+# times (the same entry point and stream)
+
+def _sample_pixels(B, Ho, Wo, n, seed):
+    rng = np.random.default_rng(seed)
+    fixed = []
+    for b in (0, B - 1):
+        for r in (0, 1, Ho // 2, Ho - 2, Ho - 1):
+            for c in (0, 1, 31, 32, 63, 64, 127, 128, Wo // 2, Wo - 2, Wo - 1):
+                if c < Wo:
+                    fixed.append((b, r, c))
+    rand = np.stack([rng.integers(0, B, n), rng.integers(0, Ho, n), rng.integers(0, Wo, n)], 1)
+    return np.concatenate([np.array(fixed, np.int64), rand.astype(np.int64)])
+
+
+def test_workload_tiny_full():
+    wl = WORKLOADS["tiny_min_tanh2"]
+    d = make_inputs(wl)
+    assert_close(run_op("min_tanh2", d), run_oracle("min_tanh2", d), what="tiny")
+
+
+def test_workload_min_tanh2_sampled():
+    wl = WORKLOADS["min_tanh2"]
+    say("generating", wl.about)
+    d = make_inputs(wl)
+    got = run_op("min_tanh2", d)
+    assert got.shape == (wl.B, 1, wl.Ho, wl.Wo)
+    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 20000, 1)
+    ref = oracle.min_tanh2_at(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(), pix)
+    assert_close(got[pix[:, 0], 0, pix[:, 1], pix[:, 2]], ref, what="min_tanh2 sampled")
+    # one whole sample, every pixel
+    full0 = oracle.min_tanh2(d["x"][:1].numpy(), d["weight"].numpy(), d["bias"].numpy())
+    assert_close(got[:1], full0, what="min_tanh2 sample 0")
+
+
+def test_workload_mul_lrelu_gelu_sampled():
+    wl = WORKLOADS["mul_lrelu_gelu"]
+    say("generating", wl.about)
+    d = make_inputs(wl)
+    got = run_op("mul_lrelu_gelu", d)
+    assert got.shape == (wl.B, wl.Cout, wl.Ho, wl.Wo)
+    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 40000, 2)
+    co = np.random.default_rng(3).integers(0, wl.Cout, pix.shape[0])
+    el = np.stack([pix[:, 0], co, pix[:, 1], pix[:, 2]], 1)
+    ref = oracle.mul_lrelu_gelu_at(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(),
+                                   d["multiplier"].numpy(), el, 0.01)
+    assert_close(got[el[:, 0], el[:, 1], el[:, 2], el[:, 3]], ref, what="mul_lrelu_gelu sampled")
+    assert np.all(np.isfinite(got))
+
+
+def test_workload_scale_min_sampled():
+    wl = WORKLOADS["scale_min"]
+    say("generating", wl.about)
+    d = make_inputs(wl)
+    got = run_op("scale_min", d, scale=2.0)
+    assert got.shape == (wl.B, 1, wl.Ho, wl.Wo)
+    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 12000, 4)
+    ref = oracle.scale_min_at(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(), pix, 2.0)
+    assert_close(got[pix[:, 0], 0, pix[:, 1], pix[:, 2]], ref, what="scale_min sampled")
+
+
+def test_workload_gn_pool_full_samples():
+    wl = WORKLOADS["gn_pool"]
+    say("generating", wl.about)
+    d = make_inputs(wl)
+    got = run_op("gn_scale_pool_clamp", d)
+    assert got.shape == (wl.B, wl.Cout, 31, 31)
+    assert got.min() >= 0.0 and got.max() <= 1.0
+    for n in (0, 77, wl.B - 1):
+        sub = {k: (v[n:n + 1] if k == "x" else v) for k, v in d.items()}
+        ref = run_oracle("gn_scale_pool_clamp", sub)
+        assert_close(got[n:n + 1], ref, what=f"gn sample {n}")
+    # widened clamp: most outputs saturate at 1 in [0, 1]; check the values
+    wide = dict(lo=-1e3, hi=1e3)
+    got_w = run_op("gn_scale_pool_clamp", d, **wide)
+    for n in (0, 64):
+        sub = {k: (v[n:n + 1] if k == "x" else v) for k, v in d.items()}
+        assert_close(got_w[n:n + 1], run_oracle("gn_scale_pool_clamp", sub, **wide),
+                     what=f"gn wide sample {n}")

@@ -1,0 +1,504 @@
+// conv3x3_igemm.hpp -- fused valid 3x3 convolution (stride 1, bias) as an
+// im2col-free implicit GEMM on the gfx950 fp32 matrix cores, with the
+// epilogue applied in registers.
+//
+// GEMM view (per sample n):
+//   C[co][p] = b[co] + sum_k A[co][k] * B[k][p]
+//   A[co][k] = w[co][ci][kh][kw],  B[k][p] = x[n][ci][r+kh][c+kw],
+//   p = (r, c) an output pixel, k = (ci, kh, kw).
+// B is never materialised: it is read out of an LDS copy of the input tile
+// plus its 2-row/2-column halo (the staging idea discussed in the
+// POPCORNBENCH l2_p54 transcript, where an input tile and a weight tile are
+// kept in shared memory).
+//
+// Work decomposition
+//   * A workgroup tile is TH output rows x TWC = 32*NCT output columns of one
+//     sample, and ALL output channels (Cout = 32*MT), so channel reductions
+//     (the min epilogues) never leave the workgroup -- they never leave the
+//     wavefront, in fact.
+//   * The tile is split into 32x32 MFMA blocks: M = 32 channels, N = 32
+//     consecutive pixels of one output row.  Each of the NWAVE wavefronts
+//     owns all MT channel blocks for NW pixel blocks ("N-tiles") that sit in
+//     one 32-column strip, NW consecutive rows.
+//   * K is walked in chunks of CC input channels (K-chunk = 9*CC).  A chunk's
+//     input tile and weight tile are copied HBM/L2 -> LDS by direct-to-LDS
+//     buffer loads (no VGPR staging) into one of two LDS stages while the
+//     matrix cores work on the other stage.
+//   * The kernel is persistent: a grid of about one workgroup per CU walks a
+//     flat stream of (tile, chunk) items, so the first chunk of the next tile
+//     is already in flight while the current tile finishes and runs its
+//     epilogue.
+//
+// MFMA v_mfma_f32_32x32x2_f32 operand layout (wave64):
+//   A (32x2): lane l supplies A[m = l%32][k = l/32]
+//   B (2x32): lane l supplies B[k = l/32][n = l%32]
+//   C (32x32): lane l, accumulator element i holds
+//              C[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32]
+// K order inside a chunk: k-step s (two k values per MFMA) is
+//   s = tap*(CC/2) + cp, tap = kh*3+kw; lane half h = l/32 takes input
+//   channel ci = 2*cp + h.  With this order every LDS address is a per-lane
+//   base plus a compile-time immediate.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace x3 {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define X3_LDS __attribute__((address_space(3)))
+
+enum Epilogue : int {
+  EPI_MIN_TANH2 = 0,       // tanh(tanh(min_co y))
+  EPI_MUL_LRELU_GELU = 1,  // gelu_erf(lrelu(y * mult[co]))
+  EPI_SCALE_MIN = 2,       // min_co(scale * y)
+  EPI_GN_POOL = 3          // GroupNorm partials + pooling-window extrema
+};
+
+// Kernel arguments (plain values, passed by value).
+struct ConvArgs {
+  const float* x;
+  const float* w;
+  const float* b;
+  float* out;
+  const float* v0;  // mult (EPI_MUL_LRELU_GELU) | gamma (EPI_GN_POOL)
+  const float* v1;  // beta  (EPI_GN_POOL)
+  const float* v2;  // scale (EPI_GN_POOL)
+  float s0;         // neg_slope (EPI_MUL_LRELU_GELU) | scale (EPI_SCALE_MIN)
+  float4* part;     // GroupNorm partials (EPI_GN_POOL)
+  int B, Cin, H, W, Cout;
+  int Ho, Wo;
+  int n_rt, n_ct;   // row tiles, column tiles per sample
+  int ntiles;       // B * n_rt * n_ct
+  int nchunk;       // ceil(Cin / CC)
+  int Ph, Pw;       // pooled output size (EPI_GN_POOL)
+  int groups;       // GroupNorm groups (EPI_GN_POOL)
+};
+
+// Compile-time geometry of one kernel configuration.
+template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_>
+struct Geo {
+  static constexpr int MT = MT_;          // 32-channel blocks (Cout = 32*MT)
+  static constexpr int CC = CC_;          // input channels per K chunk
+  static constexpr int TH = TH_;          // output rows per tile
+  static constexpr int NCT = NCT_;        // 32-column strips per tile
+  static constexpr int NWAVE = NWAVE_;
+  static constexpr int NTHR = NWAVE * 64;
+  static constexpr int COUT = 32 * MT;
+  static constexpr int TWC = 32 * NCT;    // output columns per tile
+  static constexpr int XROWS = TH + 2;    // input rows per tile (halo)
+  static constexpr int XCOLS = TWC + 2;   // input columns per tile (halo)
+  static constexpr int XP = (XCOLS + 3) / 4 * 4;  // LDS row pitch (dwords)
+  // LDS channel stride: >= XROWS*XP and == 32 (mod 64) dwords, so the two
+  // lane halves of a B-fragment read (channels ci and ci+1) use disjoint
+  // banks.
+  static constexpr int CS0 = XROWS * XP;
+  static constexpr int CS = CS0 + ((32 - (CS0 % 64)) + 64) % 64;
+  static constexpr int XBUF = CC * CS;    // input dwords per stage
+  static constexpr int KC = 9 * CC;       // K per chunk
+  static constexpr int WP = KC + 1;       // odd weight-row pitch: conflict-free
+  static constexpr int WBUF = COUT * WP;  // weight dwords per stage
+  static constexpr int STAGE = XBUF + WBUF;
+  static constexpr int LDS_DWORDS = 2 * STAGE;
+  static constexpr int KS = KC / 2;       // MFMA k-steps per chunk
+  static constexpr int NTILE_N = TH * NCT;  // N-tiles per workgroup tile
+  static constexpr int NW = NTILE_N / NWAVE;  // N-tiles per wave
+  static constexpr int NBLK = STAGE / 64;     // 64-dword LDS blocks per stage
+
+  static_assert(CC % 2 == 0, "CC must be even");
+  static_assert(NTILE_N % NWAVE == 0, "N-tiles must split evenly over waves");
+  static_assert(TH % NW == 0, "a wave's N-tiles must lie in one strip");
+  static_assert(XBUF % 64 == 0 && WBUF % 64 == 0, "stage must be 64-aligned");
+  static_assert(LDS_DWORDS * 4 <= 160 * 1024, "LDS budget exceeded");
+  static_assert(XBUF * 4 < 65536 && WBUF * 4 < 65536,
+                "ds_read immediates are 16-bit");
+};
+
+// ---------------------------------------------------------------------------
+// small device helpers
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t bytes) {
+  // Raw (un-strided) buffer: offsets >= `bytes` read as zero.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Row r of the output tile stored by the wave's N-tile j, etc.
+template <class G>
+struct WaveMap {
+  int strip;    // 32-column strip index inside the tile
+  int row0;     // first row (inside the tile) of the wave's N-tiles
+  __device__ __forceinline__ explicit WaveMap(int wave) {
+    const int first = wave * G::NW;  // N-tile index, strip-major
+    strip = first / G::TH;
+    row0 = first % G::TH;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// The kernel.
+
+template <class G, int EPI>
+__global__ void __launch_bounds__(G::NTHR)
+    conv3x3_igemm_kernel(const ConvArgs a) {
+  __shared__ float lds[G::LDS_DWORDS];
+  // Per-channel constants, loaded once: bias, and the epilogue's channel
+  // parameter (multiplier, or for the pooling path the direction flag
+  // 1 = keep the window maximum, 0 = keep the minimum).  Reading them from
+  // LDS keeps global loads out of the main loop, whose vmcnt waits would
+  // otherwise also wait for the next stage's prefetch.
+  __shared__ float s_bias[G::COUT];
+  __shared__ float s_par[G::COUT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;     // lane half
+  const int l32 = lane & 31;   // column inside an N-tile
+
+  // Persistent schedule, XCD aware: consecutive workgroup ids are spread
+  // round-robin over the 8 XCDs, so renumber them so that the workgroups
+  // resident on one XCD work on neighbouring tiles (shared halo rows and
+  // the same weights stay in that XCD's L2).
+  const int G_ = gridDim.x;
+  int vb = blockIdx.x;
+  if ((G_ & 7) == 0) vb = (blockIdx.x & 7) * (G_ >> 3) + (blockIdx.x >> 3);
+  const int my_tiles = (a.ntiles > vb) ? (a.ntiles - vb + G_ - 1) / G_ : 0;
+  const int nitems = my_tiles * a.nchunk;
+
+  const uint32_t x_sample = (uint32_t)a.Cin * a.H * a.W;  // floats
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      make_rsrc(a.w, (uint32_t)a.Cout * a.Cin * 9u * 4u);
+
+  // ---- stage one (tile, chunk) item into LDS stage `buf` ------------------
+  auto stage = [&](int item, int buf) {
+    const int tl = item / a.nchunk;
+    const int chunk = item - tl * a.nchunk;
+    const int t = vb + tl * G_;
+    const int ct = t % a.n_ct;
+    const int rt = (t / a.n_ct) % a.n_rt;
+    const int n = t / (a.n_ct * a.n_rt);
+    const int r0 = rt * G::TH, c0 = ct * G::TWC;
+    const int ci0 = chunk * G::CC;
+    const __amdgpu_buffer_rsrc_t x_rsrc =
+        make_rsrc(a.x + (size_t)n * x_sample, x_sample * 4u);
+    X3_LDS float* sbase = (X3_LDS float*)lds + buf * G::STAGE;
+#pragma unroll 1
+    for (int blk = wave; blk < G::NBLK; blk += G::NWAVE) {
+      const int p = blk * 64 + lane;
+      uint32_t off = 0x80000000u;  // out of range: the load returns 0
+      if (blk * 64 < G::XBUF) {
+        const int cil = p / G::CS;
+        const int rem = p - cil * G::CS;
+        const int row = rem / G::XP;
+        const int col = rem - row * G::XP;
+        const int ci = ci0 + cil, gr = r0 + row, gc = c0 + col;
+        const bool ok = (ci < a.Cin) & (row < G::XROWS) & (gr < a.H) &
+                        (col < G::XCOLS) & (gc < a.W);
+        off = ok ? (uint32_t)(((ci * a.H + gr) * a.W + gc) * 4) : off;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            x_rsrc, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
+      } else {
+        const int q = p - G::XBUF;
+        const int co = q / G::WP;
+        const int kk = q - co * G::WP;
+        const int ci = ci0 + kk / 9;
+        const bool ok = (kk < G::KC) & (ci < a.Cin);
+        off = ok ? (uint32_t)((co * a.Cin * 9 + ci0 * 9 + kk) * 4) : off;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            w_rsrc, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
+      }
+    }
+  };
+
+  const WaveMap<G> wm(wave);
+
+  for (int co = tid; co < G::COUT; co += G::NTHR) {
+    s_bias[co] = a.b[co];
+    float pv = 0.0f;
+    if constexpr (EPI == EPI_MUL_LRELU_GELU) pv = a.v0[co];
+    if constexpr (EPI == EPI_GN_POOL)
+      pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : 0.0f;
+    s_par[co] = pv;
+  }
+  // (made visible by the barrier at the top of the first item)
+
+  f32x16 acc[G::MT][G::NW];
+
+  if (nitems > 0) stage(0, 0);
+
+#pragma unroll 1
+  for (int item = 0; item < nitems; ++item) {
+    const int buf = item & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (item + 1 < nitems) stage(item + 1, buf ^ 1);
+
+    const int tl = item / a.nchunk;
+    const int chunk = item - tl * a.nchunk;
+    const int t = vb + tl * G_;
+
+    if (chunk == 0) {
+      // accumulators start at the bias
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float bv = s_bias[mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)];
+#pragma unroll
+          for (int j = 0; j < G::NW; ++j) acc[mt][j][i] = bv;
+        }
+    }
+
+    // ---- matrix-core main loop over the chunk ------------------------------
+    {
+      const X3_LDS float* xs = (const X3_LDS float*)lds + buf * G::STAGE +
+                               h * G::CS + wm.row0 * G::XP + wm.strip * 32 +
+                               l32;
+      const X3_LDS float* ws = (const X3_LDS float*)lds + buf * G::STAGE +
+                               G::XBUF + l32 * G::WP + h * 9;
+#pragma unroll
+      for (int s = 0; s < G::KS; ++s) {
+        const int tap = s / (G::CC / 2);
+        const int cp = s % (G::CC / 2);
+        const int kh = tap / 3, kw = tap % 3;
+        float av[G::MT], bv[G::NW];
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+          av[mt] = ws[mt * 32 * G::WP + cp * 18 + tap];
+#pragma unroll
+        for (int j = 0; j < G::NW; ++j)
+          bv[j] = xs[2 * cp * G::CS + (j + kh) * G::XP + kw];
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < G::NW; ++j)
+            acc[mt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                av[mt], bv[j], acc[mt][j], 0, 0, 0);
+      }
+    }
+
+    if (chunk != a.nchunk - 1) continue;
+
+    // ---- epilogue for tile t --------------------------------------------------
+    const int ct = t % a.n_ct;
+    const int rt = (t / a.n_ct) % a.n_rt;
+    const int n = t / (a.n_ct * a.n_rt);
+    const int r_base = rt * G::TH + wm.row0;           // output row of j = 0
+    const int c = ct * G::TWC + wm.strip * 32 + l32;   // output column
+    const bool col_ok = c < a.Wo;
+
+    if constexpr (EPI == EPI_MIN_TANH2 || EPI == EPI_SCALE_MIN) {
+      const bool use_max = (EPI == EPI_SCALE_MIN) && !(a.s0 >= 0.0f);
+#pragma unroll
+      for (int j = 0; j < G::NW; ++j) {
+        float m = acc[0][j][0];
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            m = use_max ? fmaxf(m, acc[mt][j][i]) : fminf(m, acc[mt][j][i]);
+        const float o = shfl_xor(m, 32);
+        m = use_max ? fmaxf(m, o) : fminf(m, o);
+        const int r = r_base + j;
+        if (h == 0 && col_ok && r < a.Ho) {
+          float y;
+          if constexpr (EPI == EPI_MIN_TANH2)
+            y = tanhf(tanhf(m));
+          else
+            y = a.s0 * m;
+          a.out[((size_t)n * a.Ho + r) * a.Wo + c] = y;
+        }
+      }
+    } else if constexpr (EPI == EPI_MUL_LRELU_GELU) {
+      const float slope = a.s0;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int co = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          const float mv = s_par[co];
+          float* orow = a.out + (((size_t)n * G::COUT + co) * a.Ho) * a.Wo + c;
+#pragma unroll
+          for (int j = 0; j < G::NW; ++j) {
+            float v = acc[mt][j][i] * mv;
+            v = (v >= 0.0f) ? v : slope * v;
+            const float y = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+            const int r = r_base + j;
+            if (col_ok && r < a.Ho) orow[(size_t)r * a.Wo] = y;
+          }
+        }
+    } else {  // EPI_GN_POOL: requires NW == 4, Cout/groups == 4, pool 4
+      static_assert(EPI != EPI_GN_POOL || G::NW == 4, "pool needs 4 rows");
+      // (1) GroupNorm partials of this wave: per group, sum and the sum of
+      // squared deviations from the wave-local group mean over the wave's
+      // valid pixels.  A group is 4 consecutive channels, which is exactly
+      // accumulator elements 4q..4q+3 of one lane.
+      int nrow_ok = a.Ho - r_base;
+      nrow_ok = nrow_ok < 0 ? 0 : (nrow_ok > G::NW ? G::NW : nrow_ok);
+      int ncol_ok = a.Wo - (ct * G::TWC + wm.strip * 32);
+      ncol_ok = ncol_ok < 0 ? 0 : (ncol_ok > 32 ? 32 : ncol_ok);
+      const float cnt = (float)(4 * nrow_ok * ncol_ok);
+      const float inv_cnt = cnt > 0.0f ? 1.0f / cnt : 0.0f;
+      float gsum[G::MT][4], gm2[G::MT][4];
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float s = 0.0f;
+#pragma unroll
+          for (int j = 0; j < G::NW; ++j)
+            if (col_ok && j < nrow_ok)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) s += acc[mt][j][4 * q + e];
+#pragma unroll
+          for (int msk = 1; msk < 32; msk <<= 1) s += shfl_xor(s, msk);
+          const float mean = s * inv_cnt;
+          float d2 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < G::NW; ++j)
+            if (col_ok && j < nrow_ok)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float d = acc[mt][j][4 * q + e] - mean;
+                d2 += d * d;
+              }
+#pragma unroll
+          for (int msk = 1; msk < 32; msk <<= 1) d2 += shfl_xor(d2, msk);
+          gsum[mt][q] = s;
+          gm2[mt][q] = d2;
+        }
+      {
+        // lane (h, l32 = mt*4+q) writes group g = mt*8 + 2q + h
+        float s = 0.0f, d2 = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (l32 == mt * 4 + q) {
+              s = gsum[mt][q];
+              d2 = gm2[mt][q];
+            }
+        if (l32 < G::MT * 4) {
+          const int mt = l32 >> 2, q = l32 & 3;
+          const int g = mt * 8 + 2 * q + h;
+          const int pps = a.n_rt * a.n_ct * G::NWAVE;
+          const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
+          a.part[((size_t)n * a.groups + g) * pps + slot] =
+              make_float4(s, d2, cnt, 0.0f);
+        }
+      }
+      // (2) 4x4 window extrema.  The wave's 4 N-tiles are 4 consecutive
+      // rows starting at a multiple of 4, and 4 consecutive lanes are 4
+      // consecutive columns starting at a multiple of 4, so a window is
+      // (4 rows in-lane) x (4 lanes).  Only the extremum that the monotone
+      // GroupNorm-affine-scale map sends to the window maximum is stored:
+      // the max where gamma*scale >= 0, else the min.
+      const int py = (rt * G::TH + wm.row0) >> 2;
+      const int px = (ct * G::TWC + wm.strip * 32 + l32) >> 2;
+      const bool store = ((l32 & 3) == 0) && py < a.Ph && px < a.Pw;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float mx = acc[mt][0][i], mn = acc[mt][0][i];
+#pragma unroll
+          for (int j = 1; j < G::NW; ++j) {
+            mx = fmaxf(mx, acc[mt][j][i]);
+            mn = fminf(mn, acc[mt][j][i]);
+          }
+          mx = fmaxf(mx, shfl_xor(mx, 1));
+          mn = fminf(mn, shfl_xor(mn, 1));
+          mx = fmaxf(mx, shfl_xor(mx, 2));
+          mn = fminf(mn, shfl_xor(mn, 2));
+          const int co = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (store) {
+            a.out[(((size_t)n * G::COUT + co) * a.Ph + py) * a.Pw + px] =
+                (s_par[co] != 0.0f) ? mx : mn;
+          }
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GroupNorm finalize: merge the per-wave partials of one (sample, group)
+// (Chan et al.'s pairwise update, in double), then normalize, apply the
+// affine and the per-channel scale, and clamp, in place on the pooled
+// extrema written by conv3x3_igemm_kernel<..., EPI_GN_POOL>.
+struct GnFinArgs {
+  const float4* part;
+  const float* gamma;
+  const float* beta;
+  const float* scale;
+  float* out;
+  int groups, cpg;   // groups, channels per group
+  int pps;           // partial slots per (sample, group)
+  int plane;         // Ph * Pw
+  float eps, lo, hi;
+};
+
+__device__ __forceinline__ void chan_merge(double& n, double& mean, double& m2,
+                                           double nb, double meanb,
+                                           double m2b) {
+  if (nb <= 0.0) return;
+  const double tot = n + nb;
+  const double d = meanb - mean;
+  mean += d * (nb / tot);
+  m2 += m2b + d * d * (n * nb / tot);
+  n = tot;
+}
+
+template <int NT>
+__global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
+  __shared__ double sn[NT], smean[NT], sm2[NT];
+  __shared__ float s_mean, s_rstd;
+  const int ng = blockIdx.x;  // n * groups + g
+  const int g = ng % a.groups;
+  const int tid = threadIdx.x;
+
+  double n = 0.0, mean = 0.0, m2 = 0.0;
+  const float4* p = a.part + (size_t)ng * a.pps;
+  for (int k = tid; k < a.pps; k += NT) {
+    const float4 v = p[k];
+    if (v.z > 0.0f)
+      chan_merge(n, mean, m2, (double)v.z, (double)v.x / (double)v.z,
+                 (double)v.y);
+  }
+  sn[tid] = n;
+  smean[tid] = mean;
+  sm2[tid] = m2;
+  __syncthreads();
+  for (int st = NT / 2; st > 0; st >>= 1) {
+    if (tid < st) {
+      double n0 = sn[tid], m0 = smean[tid], q0 = sm2[tid];
+      chan_merge(n0, m0, q0, sn[tid + st], smean[tid + st], sm2[tid + st]);
+      sn[tid] = n0;
+      smean[tid] = m0;
+      sm2[tid] = q0;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double var = sn[0] > 0.0 ? sm2[0] / sn[0] : 0.0;
+    s_mean = (float)smean[0];
+    s_rstd = (float)(1.0 / sqrt(var + (double)a.eps));
+  }
+  __syncthreads();
+  const float mu = s_mean, rstd = s_rstd;
+  const int total = a.cpg * a.plane;
+  float* o = a.out + (size_t)ng * total;  // channels g*cpg .. contiguous
+  for (int e = tid; e < total; e += NT) {
+    const int c = g * a.cpg + e / a.plane;
+    const float v = o[e];
+    const float z = ((v - mu) * rstd * a.gamma[c] + a.beta[c]) * a.scale[c];
+    o[e] = fminf(fmaxf(z, a.lo), a.hi);
+  }
+}
+
+}  // namespace x3
