@@ -5,6 +5,7 @@ disabled for the device code (hipcc's host pass warns that it does not know
 the feature; that warning is harmless).  No fast-math.
 """
 import os
+import re
 import subprocess
 import sys
 
@@ -28,14 +29,39 @@ def build(verbose: bool = False) -> str:
            "-I", os.path.join(PKG, "csrc"), SRC, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
+    cmd.append("-Rpass-analysis=kernel-resource-usage")
     res = subprocess.run(cmd, capture_output=True, text=True)
     # drop the host pass's harmless note about the device-only feature flag
+    # and collect the per-kernel resource remarks
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if err.strip():
-        print(err, file=sys.stderr)
+    usage, other, name = {}, [], None
+    for line in res.stderr.splitlines():
+        if noise in line:
+            continue
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            usage[name] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][^:]*?)(?: \[[^]]*\])?: (\d+) \[-Rpass", line)
+        if m and name:
+            usage[name][m.group(1)] = int(m.group(2))
+            continue
+        if "kernel-resource-usage" not in line:
+            other.append(line)
+    if "\n".join(other).strip():
+        print("\n".join(other), file=sys.stderr)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode})")
+    # A kernel that touches scratch memory has spilled registers or demoted
+    # its accumulators to memory: that is a performance bug, refuse it.
+    bad = [k for k, u in usage.items() if u.get("ScratchSize", 0) > 0]
+    if bad:
+        raise RuntimeError("kernels using scratch memory: " + ", ".join(bad))
+    if verbose:
+        for k, u in usage.items():
+            print(f"  {k[:90]}: VGPRs={u.get('VGPRs')} AGPRs={u.get('AGPRs')} "
+                  f"occupancy={u.get('Occupancy')} LDS={u.get('LDS Size')}")
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

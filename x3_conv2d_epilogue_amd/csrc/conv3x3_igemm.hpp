@@ -43,10 +43,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace x3 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define X3_LDS __attribute__((address_space(3)))
+// Every helper lambda of the kernel must inline: they capture the
+// accumulator array by reference, and an out-of-line call would force it
+// into scratch memory.
+#define X3_INLINE __attribute__((always_inline))
 
 enum Epilogue : int {
   EPI_MIN_TANH2 = 0,       // tanh(tanh(min_co y))
@@ -99,7 +105,7 @@ struct Geo {
   static constexpr int WP = KC + 1;       // odd weight-row pitch: conflict-free
   static constexpr int WBUF = COUT * WP;  // weight dwords per stage
   static constexpr int STAGE = XBUF + WBUF;
-  static constexpr int LDS_DWORDS = 2 * STAGE;
+  static constexpr int LDS_DWORDS = 2 * STAGE;  // two stages
   static constexpr int KS = KC / 2;       // MFMA k-steps per chunk
   static constexpr int NTILE_N = TH * NCT;  // N-tiles per workgroup tile
   static constexpr int NW = NTILE_N / NWAVE;  // N-tiles per wave
@@ -146,7 +152,11 @@ struct WaveMap {
 template <class G, int EPI>
 __global__ void __launch_bounds__(G::NTHR)
     conv3x3_igemm_kernel(const ConvArgs a) {
-  __shared__ float lds[G::LDS_DWORDS];
+  // Two LDS stages as two separate arrays: the direct-to-LDS loads that
+  // fill one stage are then visibly disjoint from the fragment reads of the
+  // other, so no wait is needed between them inside the MFMA loop.
+  __shared__ float lds0[G::STAGE];
+  __shared__ float lds1[G::STAGE];
   // Per-channel constants, loaded once: bias, and the epilogue's channel
   // parameter (multiplier, or for the pooling path the direction flag
   // 1 = keep the window maximum, 0 = keep the minimum).  Reading them from
@@ -175,46 +185,63 @@ __global__ void __launch_bounds__(G::NTHR)
   const __amdgpu_buffer_rsrc_t w_rsrc =
       make_rsrc(a.w, (uint32_t)a.Cout * a.Cin * 9u * 4u);
 
-  // ---- stage one (tile, chunk) item into LDS stage `buf` ------------------
-  auto stage = [&](int item, int buf) {
+  // ---- staging of one (tile, chunk) item ------------------------------------
+  // The stage is filled in 64-dword blocks, one direct-to-LDS load per block
+  // and wave (lane l writes dword l of the block); wave w owns blocks
+  // w, w + NWAVE, ...  Out-of-range elements (tile edges, channels >= Cin,
+  // row padding) are read from an offset past the buffer end and land as 0.
+  struct Item {
+    int n, r0, c0, ci0;
+  };
+  auto item_of = [&](int item) X3_INLINE {
     const int tl = item / a.nchunk;
     const int chunk = item - tl * a.nchunk;
     const int t = vb + tl * G_;
     const int ct = t % a.n_ct;
     const int rt = (t / a.n_ct) % a.n_rt;
-    const int n = t / (a.n_ct * a.n_rt);
-    const int r0 = rt * G::TH, c0 = ct * G::TWC;
-    const int ci0 = chunk * G::CC;
-    const __amdgpu_buffer_rsrc_t x_rsrc =
-        make_rsrc(a.x + (size_t)n * x_sample, x_sample * 4u);
-    X3_LDS float* sbase = (X3_LDS float*)lds + buf * G::STAGE;
-#pragma unroll 1
-    for (int blk = wave; blk < G::NBLK; blk += G::NWAVE) {
-      const int p = blk * 64 + lane;
-      uint32_t off = 0x80000000u;  // out of range: the load returns 0
-      if (blk * 64 < G::XBUF) {
-        const int cil = p / G::CS;
-        const int rem = p - cil * G::CS;
-        const int row = rem / G::XP;
-        const int col = rem - row * G::XP;
-        const int ci = ci0 + cil, gr = r0 + row, gc = c0 + col;
-        const bool ok = (ci < a.Cin) & (row < G::XROWS) & (gr < a.H) &
-                        (col < G::XCOLS) & (gc < a.W);
-        off = ok ? (uint32_t)(((ci * a.H + gr) * a.W + gc) * 4) : off;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            x_rsrc, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
-      } else {
-        const int q = p - G::XBUF;
-        const int co = q / G::WP;
-        const int kk = q - co * G::WP;
-        const int ci = ci0 + kk / 9;
-        const bool ok = (kk < G::KC) & (ci < a.Cin);
-        off = ok ? (uint32_t)((co * a.Cin * 9 + ci0 * 9 + kk) * 4) : off;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            w_rsrc, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
-      }
+    Item it;
+    it.n = t / (a.n_ct * a.n_rt);
+    it.r0 = rt * G::TH;
+    it.c0 = ct * G::TWC;
+    it.ci0 = chunk * G::CC;
+    return it;
+  };
+  auto issue = [&](const Item& it, __amdgpu_buffer_rsrc_t x_rsrc,
+                   X3_LDS float* sbase, int i) X3_INLINE {
+    const int blk = wave + i * G::NWAVE;
+    if (blk >= G::NBLK) return;
+    const int p = blk * 64 + lane;
+    uint32_t off = 0x80000000u;  // out of range: the load returns 0
+    if (blk * 64 < G::XBUF) {
+      const int cil = p / G::CS;
+      const int rem = p - cil * G::CS;
+      const int row = rem / G::XP;
+      const int col = rem - row * G::XP;
+      const int ci = it.ci0 + cil, gr = it.r0 + row, gc = it.c0 + col;
+      const bool ok = (ci < a.Cin) & (row < G::XROWS) & (gr < a.H) &
+                      (col < G::XCOLS) & (gc < a.W);
+      off = ok ? (uint32_t)(((ci * a.H + gr) * a.W + gc) * 4) : off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          x_rsrc, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
+    } else {
+      const int q = p - G::XBUF;
+      const int co = q / G::WP;
+      const int kk = q - co * G::WP;
+      const int ci = it.ci0 + kk / 9;
+      const bool ok = (kk < G::KC) & (ci < a.Cin);
+      off = ok ? (uint32_t)((co * a.Cin * 9 + it.ci0 * 9 + kk) * 4) : off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rsrc, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
     }
   };
+  auto x_rsrc_of = [&](const Item& it) X3_INLINE {
+    return make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
+  };
+  // blocks per wave per item, issued BPS per k-step over the first half of
+  // the k-steps so that they have the second half to land
+  constexpr int NB_W = (G::NBLK + G::NWAVE - 1) / G::NWAVE;
+  constexpr int KS_ISSUE = G::KS / 2 > 0 ? G::KS / 2 : 1;
+  constexpr int BPS = (NB_W + KS_ISSUE - 1) / KS_ISSUE;
 
   const WaveMap<G> wm(wave);
 
@@ -230,61 +257,7 @@ __global__ void __launch_bounds__(G::NTHR)
 
   f32x16 acc[G::MT][G::NW];
 
-  if (nitems > 0) stage(0, 0);
-
-#pragma unroll 1
-  for (int item = 0; item < nitems; ++item) {
-    const int buf = item & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (item + 1 < nitems) stage(item + 1, buf ^ 1);
-
-    const int tl = item / a.nchunk;
-    const int chunk = item - tl * a.nchunk;
-    const int t = vb + tl * G_;
-
-    if (chunk == 0) {
-      // accumulators start at the bias
-#pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float bv = s_bias[mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)];
-#pragma unroll
-          for (int j = 0; j < G::NW; ++j) acc[mt][j][i] = bv;
-        }
-    }
-
-    // ---- matrix-core main loop over the chunk ------------------------------
-    {
-      const X3_LDS float* xs = (const X3_LDS float*)lds + buf * G::STAGE +
-                               h * G::CS + wm.row0 * G::XP + wm.strip * 32 +
-                               l32;
-      const X3_LDS float* ws = (const X3_LDS float*)lds + buf * G::STAGE +
-                               G::XBUF + l32 * G::WP + h * 9;
-#pragma unroll
-      for (int s = 0; s < G::KS; ++s) {
-        const int tap = s / (G::CC / 2);
-        const int cp = s % (G::CC / 2);
-        const int kh = tap / 3, kw = tap % 3;
-        float av[G::MT], bv[G::NW];
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
-          av[mt] = ws[mt * 32 * G::WP + cp * 18 + tap];
-#pragma unroll
-        for (int j = 0; j < G::NW; ++j)
-          bv[j] = xs[2 * cp * G::CS + (j + kh) * G::XP + kw];
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-          for (int j = 0; j < G::NW; ++j)
-            acc[mt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                av[mt], bv[j], acc[mt][j], 0, 0, 0);
-      }
-    }
-
-    if (chunk != a.nchunk - 1) continue;
-
+  auto epilogue = [&](int t) X3_INLINE {
     // ---- epilogue for tile t --------------------------------------------------
     const int ct = t % a.n_ct;
     const int rt = (t / a.n_ct) % a.n_rt;
@@ -423,6 +396,90 @@ __global__ void __launch_bounds__(G::NTHR)
           }
         }
     }
+  };
+
+  // ---- one item: wait for its stage, prefetch the next item into the other
+  // stage from inside the MFMA loop, multiply, and finish the tile ----------
+  auto run_item = [&](auto bufc, int item) X3_INLINE {
+    constexpr int BUF = decltype(bufc)::value;
+    X3_LDS float* cur = BUF ? (X3_LDS float*)lds1 : (X3_LDS float*)lds0;
+    X3_LDS float* nxt = BUF ? (X3_LDS float*)lds0 : (X3_LDS float*)lds1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    const bool has_next = item + 1 < nitems;
+    const Item nit = item_of(has_next ? item + 1 : item);
+    const __amdgpu_buffer_rsrc_t nx_rsrc = x_rsrc_of(nit);
+
+    const int tl = item / a.nchunk;
+    const int chunk = item - tl * a.nchunk;
+    const int t = vb + tl * G_;
+
+    if (chunk == 0) {
+      // accumulators start at the bias
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float bv = s_bias[mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)];
+#pragma unroll
+          for (int j = 0; j < G::NW; ++j) acc[mt][j][i] = bv;
+        }
+    }
+
+    const X3_LDS float* xs =
+        cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
+    const X3_LDS float* ws = cur + G::XBUF + l32 * G::WP + h * 9;
+    // Software pipeline over the k-steps of the chunk: step s issues the LDS
+    // fragment reads of step s+1, its share of the next item's staging
+    // loads, then its MFMAs; a scheduling fence keeps that order, so each
+    // MFMA's operands were requested a full step (MT*NW MFMAs) earlier.
+    float av[2][G::MT], bv[2][G::NW];
+    auto load_frag = [&](int s, float (&A)[G::MT], float (&Bv)[G::NW]) X3_INLINE {
+      const int tap = s / (G::CC / 2);
+      const int cp = s % (G::CC / 2);
+      const int kh = tap / 3, kw = tap % 3;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+        A[mt] = ws[mt * 32 * G::WP + cp * 18 + tap];
+#pragma unroll
+      for (int j = 0; j < G::NW; ++j)
+        Bv[j] = xs[2 * cp * G::CS + (j + kh) * G::XP + kw];
+    };
+    load_frag(0, av[0], bv[0]);
+#pragma unroll
+    for (int s = 0; s < G::KS; ++s) {
+      if (s + 1 < G::KS) load_frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
+      if (has_next && s < KS_ISSUE) {
+        // a rolled loop: its uniform operands are recomputed here rather
+        // than precomputed for every step of the unrolled k-loop
+        const int i_end = (s + 1) * BPS < NB_W ? (s + 1) * BPS : NB_W;
+#pragma unroll 1
+        for (int i = __builtin_amdgcn_readfirstlane(s * BPS); i < i_end; ++i)
+          issue(nit, nx_rsrc, nxt, i);
+      }
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < G::NW; ++j)
+          acc[mt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+              av[s & 1][mt], bv[s & 1][j], acc[mt][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (chunk == a.nchunk - 1) epilogue(t);
+  };
+
+  if (nitems > 0) {
+    const Item it0 = item_of(0);
+    const __amdgpu_buffer_rsrc_t r0 = x_rsrc_of(it0);
+#pragma unroll 1
+    for (int i = 0; i < NB_W; ++i) issue(it0, r0, (X3_LDS float*)lds0, i);
+  }
+#pragma unroll 1
+  for (int item = 0; item < nitems; item += 2) {
+    run_item(std::integral_constant<int, 0>{}, item);
+    if (item + 1 < nitems) run_item(std::integral_constant<int, 1>{}, item + 1);
   }
 }
 
