@@ -29,7 +29,7 @@ def build(verbose: bool = False) -> str:
            "-I", os.path.join(PKG, "csrc"), SRC, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
-    cmd.append("-Rpass-analysis=kernel-resource-usage")
+    cmd += ["-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # drop the host pass's harmless note about the device-only feature flag
     # and collect the per-kernel resource remarks
@@ -49,7 +49,7 @@ def build(verbose: bool = False) -> str:
             continue
         if "kernel-resource-usage" not in line:
             other.append(line)
-    if "\n".join(other).strip():
+    if any(("warning" in l or "error" in l) for l in other):
         print("\n".join(other), file=sys.stderr)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode})")

@@ -104,18 +104,25 @@ struct Geo {
   static constexpr int KC = 9 * CC;       // K per chunk
   static constexpr int WP = KC + 1;       // odd weight-row pitch: conflict-free
   static constexpr int WBUF = COUT * WP;  // weight dwords per stage
-  static constexpr int STAGE = XBUF + WBUF;
+  // Both regions are padded to whole rounds of 64-dword blocks over the
+  // wavefronts, so that every wavefront stages the same number of input
+  // blocks (NBI) and weight blocks (NBW) per item, without branches.
+  static constexpr int ROUND = 64 * NWAVE;
+  static constexpr int XBUF_P = (XBUF + ROUND - 1) / ROUND * ROUND;
+  static constexpr int WBUF_P = (WBUF + ROUND - 1) / ROUND * ROUND;
+  static constexpr int NBI = XBUF_P / ROUND;  // input blocks per wave
+  static constexpr int NBW = WBUF_P / ROUND;  // weight blocks per wave
+  static constexpr int STAGE = XBUF_P + WBUF_P;
   static constexpr int LDS_DWORDS = 2 * STAGE;  // two stages
   static constexpr int KS = KC / 2;       // MFMA k-steps per chunk
   static constexpr int NTILE_N = TH * NCT;  // N-tiles per workgroup tile
   static constexpr int NW = NTILE_N / NWAVE;  // N-tiles per wave
-  static constexpr int NBLK = STAGE / 64;     // 64-dword LDS blocks per stage
 
   static_assert(CC % 2 == 0, "CC must be even");
   static_assert(NTILE_N % NWAVE == 0, "N-tiles must split evenly over waves");
   static_assert(TH % NW == 0, "a wave's N-tiles must lie in one strip");
-  static_assert(XBUF % 64 == 0 && WBUF % 64 == 0, "stage must be 64-aligned");
-  static_assert(LDS_DWORDS * 4 <= 160 * 1024, "LDS budget exceeded");
+  static_assert(LDS_DWORDS * 4 + 2 * COUT * 4 <= 160 * 1024,
+                "LDS budget exceeded");
   static_assert(XBUF * 4 < 65536 && WBUF * 4 < 65536,
                 "ds_read immediates are 16-bit");
 };
@@ -187,9 +194,10 @@ __global__ void __launch_bounds__(G::NTHR)
 
   // ---- staging of one (tile, chunk) item ------------------------------------
   // The stage is filled in 64-dword blocks, one direct-to-LDS load per block
-  // and wave (lane l writes dword l of the block); wave w owns blocks
-  // w, w + NWAVE, ...  Out-of-range elements (tile edges, channels >= Cin,
-  // row padding) are read from an offset past the buffer end and land as 0.
+  // and wave (lane l writes dword l of the block).  Wave w owns input blocks
+  // w + NWAVE*i (i < NBI) and weight blocks w + NWAVE*i (i < NBW).
+  // Out-of-range elements (tile edges, channels >= Cin, row padding) are
+  // read from an offset past the buffer end and land as 0.
   struct Item {
     int n, r0, c0, ci0;
   };
@@ -206,40 +214,73 @@ __global__ void __launch_bounds__(G::NTHR)
     it.ci0 = chunk * G::CC;
     return it;
   };
-  auto issue = [&](const Item& it, __amdgpu_buffer_rsrc_t x_rsrc,
-                   X3_LDS float* sbase, int i) X3_INLINE {
-    const int blk = wave + i * G::NWAVE;
-    if (blk >= G::NBLK) return;
-    const int p = blk * 64 + lane;
-    uint32_t off = 0x80000000u;  // out of range: the load returns 0
-    if (blk * 64 < G::XBUF) {
-      const int cil = p / G::CS;
-      const int rem = p - cil * G::CS;
-      const int row = rem / G::XP;
-      const int col = rem - row * G::XP;
-      const int ci = it.ci0 + cil, gr = it.r0 + row, gc = it.c0 + col;
-      const bool ok = (ci < a.Cin) & (row < G::XROWS) & (gr < a.H) &
-                      (col < G::XCOLS) & (gc < a.W);
-      off = ok ? (uint32_t)(((ci * a.H + gr) * a.W + gc) * 4) : off;
+  // Uniform per-item limits, computed once per item.
+  struct Lim {
+    __amdgpu_buffer_rsrc_t xr;
+    int base;      // element offset of (ci0, r0, c0) in the sample
+    int ci_lim;    // local channels < ci_lim are real
+    int row_lim;   // local rows < row_lim are real
+    int col_lim;   // local columns < col_lim are needed and real
+    int kk_lim;    // weight columns < kk_lim are real
+    int wbase;     // element offset of input channel ci0 in a weight row
+  };
+  auto lim_of = [&](const Item& it) X3_INLINE {
+    Lim l;
+    l.xr = make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
+    l.base = (it.ci0 * a.H + it.r0) * a.W + it.c0;
+    l.ci_lim = a.Cin - it.ci0;
+    const int rl = a.H - it.r0;
+    l.row_lim = rl < G::XROWS ? rl : G::XROWS;
+    const int cl = a.W - it.c0;
+    l.col_lim = cl < G::XCOLS ? cl : G::XCOLS;
+    const int kl = 9 * (a.Cin - it.ci0);
+    l.kk_lim = kl < G::KC ? kl : G::KC;
+    l.wbase = it.ci0 * 9;
+    return l;
+  };
+  const int HW = a.H * a.W, CinK = a.Cin * 9;
+  // Wave-local block i (compile-time) of the stage at `sbase`.  `zz` is an
+  // opaque per-item zero: it keeps the lane-dependent address arithmetic
+  // from being hoisted out of the item loop (which would pin one register
+  // per block for the whole kernel).
+  auto issue = [&](const Lim& l, X3_LDS float* sbase, int i, int zz)
+                   X3_INLINE {
+    // An element that must read as zero gets bit 31 set in its offset:
+    // every buffer here is smaller than 2 GiB, so such an offset is past
+    // num_records and the load returns 0.  (An OR rather than a select
+    // keeps the compiler from turning this into an exec-masked region.)
+    if (i < G::NBI) {
+      const int blk = wave + zz + i * G::NWAVE;
+      const uint32_t p = (uint32_t)(blk * 64 + lane);
+      const uint32_t cil = p / G::CS;
+      const uint32_t rem = p - cil * G::CS;
+      const uint32_t row = rem / G::XP;
+      const uint32_t col = rem - row * G::XP;
+      const bool ok = (cil < (uint32_t)l.ci_lim) &
+                      (row < (uint32_t)l.row_lim) &
+                      (col < (uint32_t)l.col_lim);
+      const uint32_t off =
+          ((cil * (uint32_t)HW + row * (uint32_t)a.W + col +
+            (uint32_t)l.base) << 2) | ((uint32_t)!ok << 31);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          x_rsrc, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
+          l.xr, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
     } else {
-      const int q = p - G::XBUF;
-      const int co = q / G::WP;
-      const int kk = q - co * G::WP;
-      const int ci = it.ci0 + kk / 9;
-      const bool ok = (kk < G::KC) & (ci < a.Cin);
-      off = ok ? (uint32_t)((co * a.Cin * 9 + it.ci0 * 9 + kk) * 4) : off;
+      const int blk = wave + zz + (i - G::NBI) * G::NWAVE;
+      const uint32_t q = (uint32_t)(blk * 64 + lane);
+      const uint32_t co = q / G::WP;
+      const uint32_t kk = q - co * G::WP;
+      const bool ok = (kk < (uint32_t)l.kk_lim) & (co < (uint32_t)G::COUT);
+      const uint32_t off =
+          ((co * (uint32_t)CinK + (uint32_t)l.wbase + kk) << 2) |
+          ((uint32_t)!ok << 31);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          w_rsrc, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
+          w_rsrc, (X3_LDS void*)(sbase + G::XBUF_P + blk * 64), 4, off, 0,
+          0, 0);
     }
   };
-  auto x_rsrc_of = [&](const Item& it) X3_INLINE {
-    return make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
-  };
-  // blocks per wave per item, issued BPS per k-step over the first half of
-  // the k-steps so that they have the second half to land
-  constexpr int NB_W = (G::NBLK + G::NWAVE - 1) / G::NWAVE;
+  // blocks per wave per item, BPS per k-step over the first half of the
+  // k-steps, so that they have the second half to land
+  constexpr int NB_W = G::NBI + G::NBW;
   constexpr int KS_ISSUE = G::KS / 2 > 0 ? G::KS / 2 : 1;
   constexpr int BPS = (NB_W + KS_ISSUE - 1) / KS_ISSUE;
 
@@ -408,8 +449,9 @@ __global__ void __launch_bounds__(G::NTHR)
     __syncthreads();
 
     const bool has_next = item + 1 < nitems;
-    const Item nit = item_of(has_next ? item + 1 : item);
-    const __amdgpu_buffer_rsrc_t nx_rsrc = x_rsrc_of(nit);
+    const Lim nl = lim_of(item_of(has_next ? item + 1 : item));
+    int zz;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
 
     const int tl = item / a.nchunk;
     const int chunk = item - tl * a.nchunk;
@@ -429,7 +471,7 @@ __global__ void __launch_bounds__(G::NTHR)
 
     const X3_LDS float* xs =
         cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
-    const X3_LDS float* ws = cur + G::XBUF + l32 * G::WP + h * 9;
+    const X3_LDS float* ws = cur + G::XBUF_P + l32 * G::WP + h * 9;
     // Software pipeline over the k-steps of the chunk: step s issues the LDS
     // fragment reads of step s+1, its share of the next item's staging
     // loads, then its MFMAs; a scheduling fence keeps that order, so each
@@ -450,13 +492,12 @@ __global__ void __launch_bounds__(G::NTHR)
 #pragma unroll
     for (int s = 0; s < G::KS; ++s) {
       if (s + 1 < G::KS) load_frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
-      if (has_next && s < KS_ISSUE) {
-        // a rolled loop: its uniform operands are recomputed here rather
-        // than precomputed for every step of the unrolled k-loop
-        const int i_end = (s + 1) * BPS < NB_W ? (s + 1) * BPS : NB_W;
-#pragma unroll 1
-        for (int i = __builtin_amdgcn_readfirstlane(s * BPS); i < i_end; ++i)
-          issue(nit, nx_rsrc, nxt, i);
+      // (unconditional: on the last item this reloads the current item's
+      // data into the idle stage, which keeps the step free of branches)
+      if (s < KS_ISSUE) {
+#pragma unroll
+        for (int u = 0; u < BPS; ++u)
+          if (s * BPS + u < NB_W) issue(nl, nxt, s * BPS + u, zz);
       }
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
@@ -464,6 +505,18 @@ __global__ void __launch_bounds__(G::NTHR)
         for (int j = 0; j < G::NW; ++j)
           acc[mt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
               av[s & 1][mt], bv[s & 1][j], acc[mt][j], 0, 0, 0);
+      // Issue order inside the step: each MFMA (64 cycles in the matrix
+      // core) is followed by a slice of this wave's other work -- LDS
+      // fragment reads, staging address arithmetic, one staging load -- so
+      // that work issues while the MFMA runs instead of between MFMA bursts.
+#pragma unroll
+      for (int k = 0; k < G::MT * G::NW; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x004, 2, 0);  // SALU
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -471,16 +524,17 @@ __global__ void __launch_bounds__(G::NTHR)
   };
 
   if (nitems > 0) {
-    const Item it0 = item_of(0);
-    const __amdgpu_buffer_rsrc_t r0 = x_rsrc_of(it0);
-#pragma unroll 1
-    for (int i = 0; i < NB_W; ++i) issue(it0, r0, (X3_LDS float*)lds0, i);
+    const Lim l0 = lim_of(item_of(0));
+#pragma unroll
+    for (int i = 0; i < NB_W; ++i) issue(l0, (X3_LDS float*)lds0, i, 0);
   }
 #pragma unroll 1
   for (int item = 0; item < nitems; item += 2) {
     run_item(std::integral_constant<int, 0>{}, item);
     if (item + 1 < nitems) run_item(std::integral_constant<int, 1>{}, item + 1);
   }
+  // the last item's (unused) prefetch must land before the LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
