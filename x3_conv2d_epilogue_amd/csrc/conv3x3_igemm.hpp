@@ -82,13 +82,16 @@ struct ConvArgs {
 };
 
 // Compile-time geometry of one kernel configuration.
-template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_>
+template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_, bool X4_>
 struct Geo {
   static constexpr int MT = MT_;          // 32-channel blocks (Cout = 32*MT)
   static constexpr int CC = CC_;          // input channels per K chunk
   static constexpr int TH = TH_;          // output rows per tile
   static constexpr int NCT = NCT_;        // 32-column strips per tile
   static constexpr int NWAVE = NWAVE_;
+  // Input rows are 16-byte aligned in memory (W % 4 == 0): stage the input
+  // with 16-byte-per-lane loads (4x fewer load instructions).
+  static constexpr bool X4 = X4_;
   static constexpr int NTHR = NWAVE * 64;
   static constexpr int COUT = 32 * MT;
   static constexpr int TWC = 32 * NCT;    // output columns per tile
@@ -104,21 +107,24 @@ struct Geo {
   static constexpr int KC = 9 * CC;       // K per chunk
   static constexpr int WP = KC + 1;       // odd weight-row pitch: conflict-free
   static constexpr int WBUF = COUT * WP;  // weight dwords per stage
-  // Both regions are padded to whole rounds of 64-dword blocks over the
-  // wavefronts, so that every wavefront stages the same number of input
-  // blocks (NBI) and weight blocks (NBW) per item, without branches.
-  static constexpr int ROUND = 64 * NWAVE;
-  static constexpr int XBUF_P = (XBUF + ROUND - 1) / ROUND * ROUND;
-  static constexpr int WBUF_P = (WBUF + ROUND - 1) / ROUND * ROUND;
-  static constexpr int NBI = XBUF_P / ROUND;  // input blocks per wave
-  static constexpr int NBW = WBUF_P / ROUND;  // weight blocks per wave
-  static constexpr int STAGE = XBUF_P + WBUF_P;
+  // Staging blocks: the input region is filled in blocks of 256 dwords
+  // (16 bytes per lane, X4) or 64 dwords (4 bytes per lane), the weight
+  // region in blocks of 64 dwords.  Every wavefront issues the same number
+  // of blocks, NBI + NBW per item; a wavefront whose turn runs past the
+  // last block reloads the last block (same data to the same place).
+  static constexpr int XBLK = X4 ? 256 : 64;
+  static constexpr int NBX = XBUF / XBLK;                 // input blocks
+  static constexpr int NBWT = WBUF / 64;                  // weight blocks
+  static constexpr int NBI = (NBX + NWAVE - 1) / NWAVE;   // per wave
+  static constexpr int NBW = (NBWT + NWAVE - 1) / NWAVE;  // per wave
+  static constexpr int STAGE = XBUF + WBUF;
   static constexpr int LDS_DWORDS = 2 * STAGE;  // two stages
   static constexpr int KS = KC / 2;       // MFMA k-steps per chunk
   static constexpr int NTILE_N = TH * NCT;  // N-tiles per workgroup tile
   static constexpr int NW = NTILE_N / NWAVE;  // N-tiles per wave
 
   static_assert(CC % 2 == 0, "CC must be even");
+  static_assert(XBUF % 256 == 0 && WBUF % 64 == 0, "whole staging blocks");
   static_assert(NTILE_N % NWAVE == 0, "N-tiles must split evenly over waves");
   static_assert(TH % NW == 0, "a wave's N-tiles must lie in one strip");
   static_assert(LDS_DWORDS * 4 + 2 * COUT * 4 <= 160 * 1024,
@@ -135,6 +141,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
   // Raw (un-strided) buffer: offsets >= `bytes` read as zero.
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            (int)bytes, 0x00020000);
+}
+
+// 16-byte-per-lane direct-to-LDS load.  The size-16 form exists only on
+// gfx950, so only the device compilation pass may see the builtin (the host
+// pass would otherwise drop the kernels that use it).
+__device__ __forceinline__ void lds_load_x4(__amdgpu_buffer_rsrc_t r,
+                                            X3_LDS void* dst, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+#endif
 }
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
@@ -193,11 +209,11 @@ __global__ void __launch_bounds__(G::NTHR)
       make_rsrc(a.w, (uint32_t)a.Cout * a.Cin * 9u * 4u);
 
   // ---- staging of one (tile, chunk) item ------------------------------------
-  // The stage is filled in 64-dword blocks, one direct-to-LDS load per block
-  // and wave (lane l writes dword l of the block).  Wave w owns input blocks
+  // The stage is filled in blocks, one direct-to-LDS load per block and
+  // wave (lane l writes piece l of the block).  Wave w owns input blocks
   // w + NWAVE*i (i < NBI) and weight blocks w + NWAVE*i (i < NBW).
-  // Out-of-range elements (tile edges, channels >= Cin, row padding) are
-  // read from an offset past the buffer end and land as 0.
+  // Elements that must be zero (rows past H, channels >= Cin, weight-row
+  // padding) are read from an offset past the buffer end and land as 0.
   struct Item {
     int n, r0, c0, ci0;
   };
@@ -250,8 +266,14 @@ __global__ void __launch_bounds__(G::NTHR)
     // num_records and the load returns 0.  (An OR rather than a select
     // keeps the compiler from turning this into an exec-masked region.)
     if (i < G::NBI) {
-      const int blk = wave + zz + i * G::NWAVE;
-      const uint32_t p = (uint32_t)(blk * 64 + lane);
+      int blk = wave + zz + i * G::NWAVE;
+      blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
+      // first dword of this lane's piece; with X4 the lane moves 4
+      // consecutive dwords of one row (XP and CS are multiples of 4, so a
+      // piece never crosses a row).  A piece whose first element is needed
+      // is loaded whole: its other elements are either needed too or lie in
+      // columns >= W - c0, which only feed masked output columns.
+      const uint32_t p = (uint32_t)(blk * G::XBLK + lane * (G::XBLK / 64));
       const uint32_t cil = p / G::CS;
       const uint32_t rem = p - cil * G::CS;
       const uint32_t row = rem / G::XP;
@@ -262,19 +284,23 @@ __global__ void __launch_bounds__(G::NTHR)
       const uint32_t off =
           ((cil * (uint32_t)HW + row * (uint32_t)a.W + col +
             (uint32_t)l.base) << 2) | ((uint32_t)!ok << 31);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          l.xr, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
+      X3_LDS void* dst = (X3_LDS void*)(sbase + blk * G::XBLK);
+      if constexpr (G::X4)
+        lds_load_x4(l.xr, dst, off);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(l.xr, dst, 4, off, 0, 0, 0);
     } else {
-      const int blk = wave + zz + (i - G::NBI) * G::NWAVE;
+      int blk = wave + zz + (i - G::NBI) * G::NWAVE;
+      blk = blk < G::NBWT - 1 ? blk : G::NBWT - 1;
       const uint32_t q = (uint32_t)(blk * 64 + lane);
       const uint32_t co = q / G::WP;
       const uint32_t kk = q - co * G::WP;
-      const bool ok = (kk < (uint32_t)l.kk_lim) & (co < (uint32_t)G::COUT);
+      const bool ok = (kk < (uint32_t)l.kk_lim);
       const uint32_t off =
           ((co * (uint32_t)CinK + (uint32_t)l.wbase + kk) << 2) |
           ((uint32_t)!ok << 31);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          w_rsrc, (X3_LDS void*)(sbase + G::XBUF_P + blk * 64), 4, off, 0,
+          w_rsrc, (X3_LDS void*)(sbase + G::XBUF + blk * 64), 4, off, 0,
           0, 0);
     }
   };
@@ -471,7 +497,7 @@ __global__ void __launch_bounds__(G::NTHR)
 
     const X3_LDS float* xs =
         cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
-    const X3_LDS float* ws = cur + G::XBUF_P + l32 * G::WP + h * 9;
+    const X3_LDS float* ws = cur + G::XBUF + l32 * G::WP + h * 9;
     // Software pipeline over the k-steps of the chunk: step s issues the LDS
     // fragment reads of step s+1, its share of the next item's staging
     // loads, then its MFMAs; a scheduling fence keeps that order, so each

@@ -111,26 +111,41 @@ x3_status run_conv(x3::ConvArgs a, hipStream_t st) {
 }
 
 // Cout = 64: 2 channel blocks x 4 N-tiles per wave, TH*NCT = 32.
-template <int EPI>
-x3_status dispatch64(const x3::ConvArgs& a, hipStream_t st) {
-  if (a.Wo > 128) return run_conv<x3::Geo<2, 8, 4, 8, 8>, EPI>(a, st);
-  if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8>, EPI>(a, st);
-  if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8>, EPI>(a, st);
-  return run_conv<x3::Geo<2, 8, 32, 1, 8>, EPI>(a, st);
+template <int EPI, bool X4>
+x3_status dispatch64_(const x3::ConvArgs& a, hipStream_t st) {
+  if (a.Wo > 128) return run_conv<x3::Geo<2, 8, 4, 8, 8, X4>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8, X4>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8, X4>, EPI>(a, st);
+  return run_conv<x3::Geo<2, 8, 32, 1, 8, X4>, EPI>(a, st);
 }
 
 // Cout = 128: 4 channel blocks x 2 N-tiles per wave, TH*NCT = 16.
+template <int EPI, bool X4>
+x3_status dispatch128_(const x3::ConvArgs& a, hipStream_t st) {
+  if (a.Wo > 128) return run_conv<x3::Geo<4, 8, 2, 8, 8, X4>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<4, 8, 4, 4, 8, X4>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<4, 8, 8, 2, 8, X4>, EPI>(a, st);
+  return run_conv<x3::Geo<4, 8, 16, 1, 8, X4>, EPI>(a, st);
+}
+
+// Input rows are 16-byte aligned when W % 4 == 0 (x itself comes from the
+// caller's allocator, checked for 16-byte alignment): then the input is
+// staged with 16-byte loads.
+bool rows_aligned16(const x3::ConvArgs& a) {
+  return (a.W % 4 == 0) && (((uintptr_t)a.x & 15u) == 0);
+}
+
 template <int EPI>
-x3_status dispatch128(const x3::ConvArgs& a, hipStream_t st) {
-  if (a.Wo > 128) return run_conv<x3::Geo<4, 8, 2, 8, 8>, EPI>(a, st);
-  if (a.Wo > 64) return run_conv<x3::Geo<4, 8, 4, 4, 8>, EPI>(a, st);
-  if (a.Wo > 32) return run_conv<x3::Geo<4, 8, 8, 2, 8>, EPI>(a, st);
-  return run_conv<x3::Geo<4, 8, 16, 1, 8>, EPI>(a, st);
+x3_status dispatch64(const x3::ConvArgs& a, hipStream_t st) {
+  return rows_aligned16(a) ? dispatch64_<EPI, true>(a, st)
+                           : dispatch64_<EPI, false>(a, st);
 }
 
 template <int EPI>
 x3_status dispatch(const x3::ConvArgs& a, hipStream_t st) {
-  return a.Cout == 64 ? dispatch64<EPI>(a, st) : dispatch128<EPI>(a, st);
+  if (a.Cout == 64) return dispatch64<EPI>(a, st);
+  return rows_aligned16(a) ? dispatch128_<EPI, true>(a, st)
+                           : dispatch128_<EPI, false>(a, st);
 }
 
 x3::ConvArgs base_args(const float* x, const float* w, const float* b,
