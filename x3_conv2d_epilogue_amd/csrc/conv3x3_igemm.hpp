@@ -157,6 +157,41 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// DPP lane permutations (within rows of 16 lanes), applied to a float.
+enum : int {
+  DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
+  DPP_QUAD_XOR2 = 0x4E,  // quad_perm [2,3,0,1]
+  DPP_ROW_ROR4 = 0x124,  // rotate a row of 16 by 4
+  DPP_ROW_ROR8 = 0x128   // rotate a row of 16 by 8
+};
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                         0xF, 0xF, false));
+}
+// Lane l <-> l ^ 16 inside each half-wave (ds_swizzle bit mode:
+// and_mask 0x1F, xor_mask 0x10).
+__device__ __forceinline__ float swz_xor16(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+// The value lane 0 holds (for lanes 0..31) or lane 32 holds (lanes 32..63).
+__device__ __forceinline__ float half_lane0(float v, int h) {
+  const int bits = __builtin_bit_cast(int, v);
+  const int lo = __builtin_amdgcn_readlane(bits, 0);
+  const int hi = __builtin_amdgcn_readlane(bits, 32);
+  return __builtin_bit_cast(float, h ? hi : lo);
+}
+// Sum over the 32 lanes of a half-wave, returned to every lane of it.
+__device__ __forceinline__ float sum32(float v) {
+  v += dpp<DPP_QUAD_XOR1>(v);
+  v += dpp<DPP_QUAD_XOR2>(v);
+  v += dpp<DPP_ROW_ROR4>(v);
+  v += dpp<DPP_ROW_ROR8>(v);
+  return v + swz_xor16(v);
+}
+
 // Row r of the output tile stored by the wave's N-tile j, etc.
 template <class G>
 struct WaveMap {
@@ -375,10 +410,13 @@ __global__ void __launch_bounds__(G::NTHR)
         }
     } else {  // EPI_GN_POOL: requires NW == 4, Cout/groups == 4, pool 4
       static_assert(EPI != EPI_GN_POOL || G::NW == 4, "pool needs 4 rows");
-      // (1) GroupNorm partials of this wave: per group, sum and the sum of
-      // squared deviations from the wave-local group mean over the wave's
-      // valid pixels.  A group is 4 consecutive channels, which is exactly
-      // accumulator elements 4q..4q+3 of one lane.
+      // (1) GroupNorm partials of this wave: per group, the count, the sum
+      // and the sum of squared deviations from the wave's own group mean,
+      // over the wave's valid pixels.  A group is 4 consecutive channels,
+      // which is exactly accumulator elements 4q..4q+3 of one lane.  The
+      // deviations are taken in one pass from a shift K, a conv value of
+      // the same group (so |mean - K| is of the order of the spread):
+      // S1 = sum(x - K), S2 = sum((x - K)^2), M2 = S2 - S1^2 / n.
       int nrow_ok = a.Ho - r_base;
       nrow_ok = nrow_ok < 0 ? 0 : (nrow_ok > G::NW ? G::NW : nrow_ok);
       int ncol_ok = a.Wo - (ct * G::TWC + wm.strip * 32);
@@ -390,28 +428,23 @@ __global__ void __launch_bounds__(G::NTHR)
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float s = 0.0f;
-#pragma unroll
-          for (int j = 0; j < G::NW; ++j)
-            if (col_ok && j < nrow_ok)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) s += acc[mt][j][4 * q + e];
-#pragma unroll
-          for (int msk = 1; msk < 32; msk <<= 1) s += shfl_xor(s, msk);
-          const float mean = s * inv_cnt;
-          float d2 = 0.0f;
+          // shift: the value lane 0 (half 0) / lane 32 (half 1) holds for
+          // the group's first channel in its first N-tile (always finite)
+          const float K = half_lane0(acc[mt][0][4 * q], h);
+          float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
           for (int j = 0; j < G::NW; ++j)
             if (col_ok && j < nrow_ok)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const float d = acc[mt][j][4 * q + e] - mean;
-                d2 += d * d;
+                const float d = acc[mt][j][4 * q + e] - K;
+                s1 += d;
+                s2 += d * d;
               }
-#pragma unroll
-          for (int msk = 1; msk < 32; msk <<= 1) d2 += shfl_xor(d2, msk);
-          gsum[mt][q] = s;
-          gm2[mt][q] = d2;
+          s1 = sum32(s1);
+          s2 = sum32(s2);
+          gsum[mt][q] = K * cnt + s1;
+          gm2[mt][q] = fmaxf(s2 - s1 * s1 * inv_cnt, 0.0f);
         }
       {
         // lane (h, l32 = mt*4+q) writes group g = mt*8 + 2q + h
@@ -452,10 +485,10 @@ __global__ void __launch_bounds__(G::NTHR)
             mx = fmaxf(mx, acc[mt][j][i]);
             mn = fminf(mn, acc[mt][j][i]);
           }
-          mx = fmaxf(mx, shfl_xor(mx, 1));
-          mn = fminf(mn, shfl_xor(mn, 1));
-          mx = fmaxf(mx, shfl_xor(mx, 2));
-          mn = fminf(mn, shfl_xor(mn, 2));
+          mx = fmaxf(mx, dpp<DPP_QUAD_XOR1>(mx));
+          mn = fminf(mn, dpp<DPP_QUAD_XOR1>(mn));
+          mx = fmaxf(mx, dpp<DPP_QUAD_XOR2>(mx));
+          mn = fminf(mn, dpp<DPP_QUAD_XOR2>(mn));
           const int co = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
           if (store) {
             a.out[(((size_t)n * G::COUT + co) * a.Ph + py) * a.Pw + px] =
