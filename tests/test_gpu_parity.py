@@ -347,3 +347,30 @@ def test_workload_gn_pool_full_samples():
         sub = {k: (v[n:n + 1] if k == "x" else v) for k, v in d.items()}
         assert_close(got_w[n:n + 1], run_oracle("gn_scale_pool_clamp", sub, **wide),
                      what=f"gn wide sample {n}")
+
+
+def test_misaligned_buffers_take_the_scalar_paths():
+    """x and out 4 bytes off 16-byte alignment: the kernels fall back to
+    dword input staging and the scalar GroupNorm finalize."""
+    d = random_case("gn_scale_pool_clamp", 2, 8, 30, 36, 64, seed=950)
+    g = to_dev(d)
+    nx = g["x"].numel()
+    xb = torch.empty(nx + 1, device=DEV)
+    xb[1:].copy_(g["x"].reshape(-1))
+    xm = xb[1:].view_as(g["x"])
+    assert xm.data_ptr() % 16 == 4
+    m = 2 * 64 * 7 * 8
+    ob = torch.empty(m + 1, device=DEV)
+    om = ob[1:].view(2, 64, 7, 8)
+    x3.conv3x3_gn_scale_pool_clamp(xm, g["weight"], g["bias"], g["gamma"], g["beta"],
+                                   g["scale"], lo=-50.0, hi=50.0, out=om)
+    torch.cuda.synchronize()
+    assert_close(om.cpu().numpy(), run_oracle("gn_scale_pool_clamp", d, lo=-50.0, hi=50.0),
+                 what="gn misaligned")
+    d2 = random_case("scale_min", 1, 12, 14, 64, 128, seed=951)
+    g2 = to_dev(d2)
+    xb2 = torch.empty(g2["x"].numel() + 1, device=DEV)
+    xb2[1:].copy_(g2["x"].reshape(-1))
+    out = x3.conv3x3_scale_min(xb2[1:].view_as(g2["x"]), g2["weight"], g2["bias"], 2.0)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), run_oracle("scale_min", d2), what="x misaligned")

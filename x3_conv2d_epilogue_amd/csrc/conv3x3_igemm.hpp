@@ -598,9 +598,9 @@ __global__ void __launch_bounds__(G::NTHR)
 
 // ---------------------------------------------------------------------------
 // GroupNorm finalize: merge the per-wave partials of one (sample, group)
-// (Chan et al.'s pairwise update, in double), then normalize, apply the
-// affine and the per-channel scale, and clamp, in place on the pooled
-// extrema written by conv3x3_igemm_kernel<..., EPI_GN_POOL>.
+// in double, then normalize, apply the affine and the per-channel scale,
+// and clamp, in place on the pooled extrema written by
+// conv3x3_igemm_kernel<..., EPI_GN_POOL>.
 struct GnFinArgs {
   const float4* part;
   const float* gamma;
@@ -611,64 +611,114 @@ struct GnFinArgs {
   int pps;           // partial slots per (sample, group)
   int plane;         // Ph * Pw
   float eps, lo, hi;
+  double count;      // elements per group: cpg * Ho * Wo
 };
 
-__device__ __forceinline__ void chan_merge(double& n, double& mean, double& m2,
-                                           double nb, double meanb,
-                                           double m2b) {
-  if (nb <= 0.0) return;
-  const double tot = n + nb;
-  const double d = meanb - mean;
-  mean += d * (nb / tot);
-  m2 += m2b + d * d * (n * nb / tot);
-  n = tot;
+// Sum of a double over the workgroup (wave shuffles, then LDS); every
+// thread gets the total.  `red` holds one slot per wavefront.
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double* red) {
+#pragma unroll
+  for (int mask = 1; mask < 64; mask <<= 1) v += __shfl_xor(v, mask, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) t += red[w];
+  return t;
 }
 
-template <int NT>
+// One workgroup of NT threads per (sample, group).  The group's 4 pooled
+// channel planes are one contiguous block of 4*plane floats in `out`; with
+// VEC (block 16-byte aligned) it is moved as float4.
+//
+// Merge: every partial k holds (sum_k, M2_k, n_k) over its pixels, with
+// M2_k taken about its own mean.  With N = sum n_k (known: channels x Ho x
+// Wo), mean = sum_k sum_k / N and M2 = sum_k [M2_k + n_k (sum_k/n_k -
+// mean)^2] (the parallel-variance combination of Chan, Golub and LeVeque),
+// accumulated in double.
+template <int NT, bool VEC>
 __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
-  __shared__ double sn[NT], smean[NT], sm2[NT];
-  __shared__ float s_mean, s_rstd;
+  static_assert(NT % 64 == 0 && NT <= 1024, "whole wavefronts");
+  __shared__ double red0[NT / 64], red1[NT / 64];
   const int ng = blockIdx.x;  // n * groups + g
   const int g = ng % a.groups;
   const int tid = threadIdx.x;
-
-  double n = 0.0, mean = 0.0, m2 = 0.0;
+  const int total = a.cpg * a.plane;  // floats in the block
+  float* o = a.out + (size_t)ng * total;
+  const int nvec = VEC ? total / 4 : total;
   const float4* p = a.part + (size_t)ng * a.pps;
-  for (int k = tid; k < a.pps; k += NT) {
+
+  const float4 p0 = tid < a.pps ? p[tid] : make_float4(0.f, 0.f, 0.f, 0.f);
+  // this thread's first block element, requested now so that its latency
+  // hides behind the statistics merge below
+  float4 first = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tid < nvec) {
+    if constexpr (VEC)
+      first = reinterpret_cast<const float4*>(o)[tid];
+    else
+      first.x = o[tid];
+  }
+  double sum = (double)p0.x;
+  for (int k = tid + NT; k < a.pps; k += NT) sum += (double)p[k].x;
+  const double mean = block_sum<NT>(sum, red0) / a.count;
+  double m2 = 0.0;
+  if (p0.z > 0.0f) {
+    const double d = (double)p0.x / (double)p0.z - mean;
+    m2 = (double)p0.y + (double)p0.z * d * d;
+  }
+  for (int k = tid + NT; k < a.pps; k += NT) {
     const float4 v = p[k];
-    if (v.z > 0.0f)
-      chan_merge(n, mean, m2, (double)v.z, (double)v.x / (double)v.z,
-                 (double)v.y);
-  }
-  sn[tid] = n;
-  smean[tid] = mean;
-  sm2[tid] = m2;
-  __syncthreads();
-  for (int st = NT / 2; st > 0; st >>= 1) {
-    if (tid < st) {
-      double n0 = sn[tid], m0 = smean[tid], q0 = sm2[tid];
-      chan_merge(n0, m0, q0, sn[tid + st], smean[tid + st], sm2[tid + st]);
-      sn[tid] = n0;
-      smean[tid] = m0;
-      sm2[tid] = q0;
+    if (v.z > 0.0f) {
+      const double d = (double)v.x / (double)v.z - mean;
+      m2 += (double)v.y + (double)v.z * d * d;
     }
-    __syncthreads();
   }
-  if (tid == 0) {
-    const double var = sn[0] > 0.0 ? sm2[0] / sn[0] : 0.0;
-    s_mean = (float)smean[0];
-    s_rstd = (float)(1.0 / sqrt(var + (double)a.eps));
+  m2 = block_sum<NT>(m2, red1);
+  const float mu = (float)mean;
+  const float rstd = (float)(1.0 / sqrt(m2 / a.count + (double)a.eps));
+
+  // z = ((v - mu) * rstd * gamma + beta) * scale = (v - mu) * A + Bc, with
+  // A = rstd*gamma*scale and Bc = beta*scale per channel; monotone in v
+  // with the sign of gamma*scale, as the pooling pass assumed.
+  // Per-channel constants as plain scalars, selected per element (an
+  // indexed array or struct here ends up in LDS or scratch memory).
+  const int c0 = g * a.cpg;
+  const int c1 = c0 + (a.cpg > 1), c2 = c0 + 2 * (a.cpg > 2),
+            c3 = c0 + 3 * (a.cpg > 3);
+  const float A0 = rstd * a.gamma[c0] * a.scale[c0];
+  const float A1 = rstd * a.gamma[c1] * a.scale[c1];
+  const float A2 = rstd * a.gamma[c2] * a.scale[c2];
+  const float A3 = rstd * a.gamma[c3] * a.scale[c3];
+  const float B0 = a.beta[c0] * a.scale[c0];
+  const float B1 = a.beta[c1] * a.scale[c1];
+  const float B2 = a.beta[c2] * a.scale[c2];
+  const float B3 = a.beta[c3] * a.scale[c3];
+  const int p1 = a.plane, p2 = 2 * a.plane, p3 = 3 * a.plane;
+  const float lo = a.lo, hi = a.hi;
+#define X3_GN_OUT(v, e)                                                     \
+  fminf(fmaxf(fmaf((v) - mu,                                                \
+                   (e) < p1 ? A0 : ((e) < p2 ? A1 : ((e) < p3 ? A2 : A3)), \
+                   (e) < p1 ? B0 : ((e) < p2 ? B1 : ((e) < p3 ? B2 : B3))), \
+              lo),                                                          \
+        hi)
+  for (int k = tid; k < nvec; k += NT) {
+    if constexpr (VEC) {
+      const float4 v =
+          k == tid ? first : reinterpret_cast<const float4*>(o)[k];
+      const int e = 4 * k;
+      float4 r;
+      r.x = X3_GN_OUT(v.x, e);
+      r.y = X3_GN_OUT(v.y, e + 1);
+      r.z = X3_GN_OUT(v.z, e + 2);
+      r.w = X3_GN_OUT(v.w, e + 3);
+      reinterpret_cast<float4*>(o)[k] = r;
+    } else {
+      const float v = k == tid ? first.x : o[k];
+      o[k] = X3_GN_OUT(v, k);
+    }
   }
-  __syncthreads();
-  const float mu = s_mean, rstd = s_rstd;
-  const int total = a.cpg * a.plane;
-  float* o = a.out + (size_t)ng * total;  // channels g*cpg .. contiguous
-  for (int e = tid; e < total; e += NT) {
-    const int c = g * a.cpg + e / a.plane;
-    const float v = o[e];
-    const float z = ((v - mu) * rstd * a.gamma[c] + a.beta[c]) * a.scale[c];
-    o[e] = fminf(fmaxf(z, a.lo), a.hi);
-  }
+#undef X3_GN_OUT
 }
 
 }  // namespace x3

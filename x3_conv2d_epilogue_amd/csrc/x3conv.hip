@@ -342,8 +342,16 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   f.eps = eps;
   f.lo = lo;
   f.hi = hi;
-  hipLaunchKernelGGL((x3::gn_finalize_kernel<256>), dim3((unsigned)(B * groups)),
-                     dim3(256), 0, st, f);
+  f.count = (double)f.cpg * s.Ho * s.Wo;
+  // The finalize moves each group's pooled block as float4 when it is
+  // 16-byte aligned (4 channels per group make every block a multiple of 4
+  // floats; `out` itself must be aligned).
+  if (((uintptr_t)out & 15u) == 0 && (f.cpg * f.plane) % 4 == 0)
+    hipLaunchKernelGGL((x3::gn_finalize_kernel<256, true>),
+                       dim3((unsigned)(B * groups)), dim3(256), 0, st, f);
+  else
+    hipLaunchKernelGGL((x3::gn_finalize_kernel<256, false>),
+                       dim3((unsigned)(B * groups)), dim3(256), 0, st, f);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(X3_EHIP, "finalize kernel launch failed: %s",
