@@ -157,6 +157,26 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// erf for the exact-GELU epilogue, by formula 7.1.26 of Abramowitz and
+// Stegun, Handbook of Mathematical Functions: for x >= 0,
+//   erf(x) ~ 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x),
+// with absolute error at most 1.5e-7; erf is odd.  Costs one reciprocal,
+// one exp2 and six FMAs.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float q = 1.061405429f;
+  q = fmaf(q, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  q *= t;
+  // exp(-x^2) = 2^(-x^2 * log2(e))
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return copysignf(fmaf(-q, e, 1.0f), x);
+}
+
 // DPP lane permutations (within rows of 16 lanes), applied to a float.
 enum : int {
   DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
@@ -369,26 +389,36 @@ __global__ void __launch_bounds__(G::NTHR)
     const bool col_ok = c < a.Wo;
 
     if constexpr (EPI == EPI_MIN_TANH2 || EPI == EPI_SCALE_MIN) {
+      // Channel extremum per pixel: in-lane over the lane's 16*MT channels,
+      // then across the two lane halves (which hold the other channels of
+      // the same pixels).  Half 0 finishes pixel rows 0..NW/2-1 and half 1
+      // rows NW/2..NW-1, so every lane evaluates and stores NW/2 results.
+      static_assert(G::NW % 2 == 0, "lane halves split the N-tiles");
+      constexpr int HN = G::NW / 2;
       const bool use_max = (EPI == EPI_SCALE_MIN) && !(a.s0 >= 0.0f);
+      float m[G::NW];
 #pragma unroll
       for (int j = 0; j < G::NW; ++j) {
-        float m = acc[0][j][0];
+        float v = acc[0][j][0];
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            m = use_max ? fmaxf(m, acc[mt][j][i]) : fminf(m, acc[mt][j][i]);
-        const float o = shfl_xor(m, 32);
-        m = use_max ? fmaxf(m, o) : fminf(m, o);
-        const int r = r_base + j;
-        if (h == 0 && col_ok && r < a.Ho) {
-          float y;
-          if constexpr (EPI == EPI_MIN_TANH2)
-            y = tanhf(tanhf(m));
-          else
-            y = a.s0 * m;
-          a.out[((size_t)n * a.Ho + r) * a.Wo + c] = y;
-        }
+            v = use_max ? fmaxf(v, acc[mt][j][i]) : fminf(v, acc[mt][j][i]);
+        m[j] = v;
+      }
+#pragma unroll
+      for (int jj = 0; jj < HN; ++jj) {
+        const float keep = h ? m[jj + HN] : m[jj];
+        const float recv = shfl_xor(h ? m[jj] : m[jj + HN], 32);
+        const float v = use_max ? fmaxf(keep, recv) : fminf(keep, recv);
+        const int r = r_base + jj + h * HN;
+        float y;
+        if constexpr (EPI == EPI_MIN_TANH2)
+          y = tanhf(tanhf(v));
+        else
+          y = a.s0 * v;
+        if (col_ok && r < a.Ho) a.out[((size_t)n * a.Ho + r) * a.Wo + c] = y;
       }
     } else if constexpr (EPI == EPI_MUL_LRELU_GELU) {
       const float slope = a.s0;
@@ -403,7 +433,7 @@ __global__ void __launch_bounds__(G::NTHR)
           for (int j = 0; j < G::NW; ++j) {
             float v = acc[mt][j][i] * mv;
             v = (v >= 0.0f) ? v : slope * v;
-            const float y = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+            const float y = 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
             const int r = r_base + j;
             if (col_ok && r < a.Ho) orow[(size_t)r * a.Wo] = y;
           }
