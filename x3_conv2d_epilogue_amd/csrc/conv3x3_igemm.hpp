@@ -48,6 +48,7 @@
 namespace x3 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define X3_LDS __attribute__((address_space(3)))
 // Every helper lambda of the kernel must inline: they capture the
 // accumulator array by reference, and an out-of-line call would force it
@@ -82,7 +83,8 @@ struct ConvArgs {
 };
 
 // Compile-time geometry of one kernel configuration.
-template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_, bool X4_>
+template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_, bool X4_,
+          bool RESW_ = false>
 struct Geo {
   static constexpr int MT = MT_;          // 32-channel blocks (Cout = 32*MT)
   static constexpr int CC = CC_;          // input channels per K chunk
@@ -92,6 +94,9 @@ struct Geo {
   // Input rows are 16-byte aligned in memory (W % 4 == 0): stage the input
   // with 16-byte-per-lane loads (4x fewer load instructions).
   static constexpr bool X4 = X4_;
+  // The weight tile stays resident in LDS for the whole kernel (only valid
+  // when K fits one chunk, Cin <= CC); items then stage the input only.
+  static constexpr bool RESW = RESW_;
   static constexpr int NTHR = NWAVE * 64;
   static constexpr int COUT = 32 * MT;
   static constexpr int TWC = 32 * NCT;    // output columns per tile
@@ -117,8 +122,10 @@ struct Geo {
   static constexpr int NBWT = WBUF / 64;                  // weight blocks
   static constexpr int NBI = (NBX + NWAVE - 1) / NWAVE;   // per wave
   static constexpr int NBW = (NBWT + NWAVE - 1) / NWAVE;  // per wave
-  static constexpr int STAGE = XBUF + WBUF;
-  static constexpr int LDS_DWORDS = 2 * STAGE;  // two stages
+  static constexpr int STAGE = XBUF + (RESW ? 0 : WBUF);
+  static constexpr int LDS_DWORDS = 2 * STAGE + (RESW ? WBUF : 0);
+  // blocks each wave stages per item
+  static constexpr int NB_ITEM = NBI + (RESW ? 0 : NBW);
   static constexpr int KS = KC / 2;       // MFMA k-steps per chunk
   static constexpr int NTILE_N = TH * NCT;  // N-tiles per workgroup tile
   static constexpr int NW = NTILE_N / NWAVE;  // N-tiles per wave
@@ -229,12 +236,14 @@ struct WaveMap {
 
 template <class G, int EPI>
 __global__ void __launch_bounds__(G::NTHR)
+    __attribute__((amdgpu_waves_per_eu(2, 2)))
     conv3x3_igemm_kernel(const ConvArgs a) {
   // Two LDS stages as two separate arrays: the direct-to-LDS loads that
   // fill one stage are then visibly disjoint from the fragment reads of the
   // other, so no wait is needed between them inside the MFMA loop.
   __shared__ float lds0[G::STAGE];
   __shared__ float lds1[G::STAGE];
+  __shared__ float ldsw[G::RESW ? G::WBUF : 1];  // resident weight tile
   // Per-channel constants, loaded once: bias, and the epilogue's channel
   // parameter (multiplier, or for the pooling path the direction flag
   // 1 = keep the window maximum, 0 = keep the minimum).  Reading them from
@@ -354,14 +363,14 @@ __global__ void __launch_bounds__(G::NTHR)
       const uint32_t off =
           ((co * (uint32_t)CinK + (uint32_t)l.wbase + kk) << 2) |
           ((uint32_t)!ok << 31);
+      X3_LDS float* wdst = G::RESW ? (X3_LDS float*)ldsw : sbase + G::XBUF;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          w_rsrc, (X3_LDS void*)(sbase + G::XBUF + blk * 64), 4, off, 0,
-          0, 0);
+          w_rsrc, (X3_LDS void*)(wdst + blk * 64), 4, off, 0, 0, 0);
     }
   };
   // blocks per wave per item, BPS per k-step over the first half of the
   // k-steps, so that they have the second half to land
-  constexpr int NB_W = G::NBI + G::NBW;
+  constexpr int NB_W = G::NB_ITEM;
   constexpr int KS_ISSUE = G::KS / 2 > 0 ? G::KS / 2 : 1;
   constexpr int BPS = (NB_W + KS_ISSUE - 1) / KS_ISSUE;
 
@@ -440,6 +449,17 @@ __global__ void __launch_bounds__(G::NTHR)
         }
     } else {  // EPI_GN_POOL: requires NW == 4, Cout/groups == 4, pool 4
       static_assert(EPI != EPI_GN_POOL || G::NW == 4, "pool needs 4 rows");
+      // Stores go through raw buffer resources over this sample's slice of
+      // `part` and `out`; a store that must not happen gets bit 31 set in
+      // its offset (past num_records, dropped by the hardware), so the
+      // epilogue has no exec-masked branches.
+      const int PP = a.Ph * a.Pw;
+      const int pps = a.n_rt * a.n_ct * G::NWAVE;
+      const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
+          a.out + (size_t)n * G::COUT * PP, (uint32_t)(G::COUT * PP * 4));
+      const __amdgpu_buffer_rsrc_t p_rsrc =
+          make_rsrc(a.part + (size_t)n * a.groups * pps,
+                    (uint32_t)(a.groups * pps * 16));
       // (1) GroupNorm partials of this wave: per group, the count, the sum
       // and the sum of squared deviations from the wave's own group mean,
       // over the wave's valid pixels.  A group is 4 consecutive channels,
@@ -453,77 +473,78 @@ __global__ void __launch_bounds__(G::NTHR)
       ncol_ok = ncol_ok < 0 ? 0 : (ncol_ok > 32 ? 32 : ncol_ok);
       const float cnt = (float)(4 * nrow_ok * ncol_ok);
       const float inv_cnt = cnt > 0.0f ? 1.0f / cnt : 0.0f;
-      float gsum[G::MT][4], gm2[G::MT][4];
+      float my_sum = 0.0f, my_m2 = 0.0f;  // lane l32 = mt*4+q keeps (mt, q)
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          // shift: the value lane 0 (half 0) / lane 32 (half 1) holds for
-          // the group's first channel in its first N-tile (always finite)
           const float K = half_lane0(acc[mt][0][4 * q], h);
           float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-          for (int j = 0; j < G::NW; ++j)
-            if (col_ok && j < nrow_ok)
+          for (int j = 0; j < G::NW; ++j) {
+            const bool ok = col_ok && j < nrow_ok;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float d = acc[mt][j][4 * q + e] - K;
-                s1 += d;
-                s2 += d * d;
-              }
+            for (int e = 0; e < 4; ++e) {
+              const float d = ok ? acc[mt][j][4 * q + e] - K : 0.0f;
+              s1 += d;
+              s2 = fmaf(d, d, s2);
+            }
+          }
           s1 = sum32(s1);
           s2 = sum32(s2);
-          gsum[mt][q] = K * cnt + s1;
-          gm2[mt][q] = fmaxf(s2 - s1 * s1 * inv_cnt, 0.0f);
+          const bool mine = l32 == mt * 4 + q;
+          my_sum = mine ? fmaf(K, cnt, s1) : my_sum;
+          my_m2 = mine ? fmaxf(s2 - s1 * s1 * inv_cnt, 0.0f) : my_m2;
         }
       {
         // lane (h, l32 = mt*4+q) writes group g = mt*8 + 2q + h
-        float s = 0.0f, d2 = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (l32 == mt * 4 + q) {
-              s = gsum[mt][q];
-              d2 = gm2[mt][q];
-            }
-        if (l32 < G::MT * 4) {
-          const int mt = l32 >> 2, q = l32 & 3;
-          const int g = mt * 8 + 2 * q + h;
-          const int pps = a.n_rt * a.n_ct * G::NWAVE;
-          const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
-          a.part[((size_t)n * a.groups + g) * pps + slot] =
-              make_float4(s, d2, cnt, 0.0f);
-        }
+        const int g = (l32 >> 2) * 8 + 2 * (l32 & 3) + h;
+        const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
+        const uint32_t off = ((uint32_t)(g * pps + slot) << 4) |
+                             ((uint32_t)(l32 >= G::MT * 4) << 31);
+        const float4 v = make_float4(my_sum, my_m2, cnt, 0.0f);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, v), p_rsrc, off, 0, 0);
       }
       // (2) 4x4 window extrema.  The wave's 4 N-tiles are 4 consecutive
       // rows starting at a multiple of 4, and 4 consecutive lanes are 4
       // consecutive columns starting at a multiple of 4, so a window is
-      // (4 rows in-lane) x (4 lanes).  Only the extremum that the monotone
-      // GroupNorm-affine-scale map sends to the window maximum is stored:
-      // the max where gamma*scale >= 0, else the min.
+      // (4 rows in-lane) x (4 lanes).  After the quad reduction all 4 lanes
+      // of a quad hold the window's value for every channel, so lane e of
+      // the quad stores channel 4-block element e.  Only the extremum that
+      // the monotone GroupNorm-affine-scale map sends to the window maximum
+      // is stored: the max where gamma*scale >= 0, else the min.
       const int py = (rt * G::TH + wm.row0) >> 2;
       const int px = (ct * G::TWC + wm.strip * 32 + l32) >> 2;
-      const bool store = ((l32 & 3) == 0) && py < a.Ph && px < a.Pw;
+      const uint32_t win_off = (uint32_t)(py * a.Pw + px);
+      const uint32_t win_bad = (uint32_t)!(py < a.Ph && px < a.Pw) << 31;
+      const int e = l32 & 3;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float mx = acc[mt][0][i], mn = acc[mt][0][i];
+        for (int q = 0; q < 4; ++q) {
+          float mx[4], mn[4];
 #pragma unroll
-          for (int j = 1; j < G::NW; ++j) {
-            mx = fmaxf(mx, acc[mt][j][i]);
-            mn = fminf(mn, acc[mt][j][i]);
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int i = 4 * q + e2;
+            float x = acc[mt][0][i], y = acc[mt][0][i];
+#pragma unroll
+            for (int j = 1; j < G::NW; ++j) {
+              x = fmaxf(x, acc[mt][j][i]);
+              y = fminf(y, acc[mt][j][i]);
+            }
+            x = fmaxf(x, dpp<DPP_QUAD_XOR1>(x));
+            y = fminf(y, dpp<DPP_QUAD_XOR1>(y));
+            mx[e2] = fmaxf(x, dpp<DPP_QUAD_XOR2>(x));
+            mn[e2] = fminf(y, dpp<DPP_QUAD_XOR2>(y));
           }
-          mx = fmaxf(mx, dpp<DPP_QUAD_XOR1>(mx));
-          mn = fminf(mn, dpp<DPP_QUAD_XOR1>(mn));
-          mx = fmaxf(mx, dpp<DPP_QUAD_XOR2>(mx));
-          mn = fminf(mn, dpp<DPP_QUAD_XOR2>(mn));
-          const int co = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (store) {
-            a.out[(((size_t)n * G::COUT + co) * a.Ph + py) * a.Pw + px] =
-                (s_par[co] != 0.0f) ? mx : mn;
-          }
+          const float vmx = e == 0 ? mx[0] : (e == 1 ? mx[1] : (e == 2 ? mx[2] : mx[3]));
+          const float vmn = e == 0 ? mn[0] : (e == 1 ? mn[1] : (e == 2 ? mn[2] : mn[3]));
+          const int co = mt * 32 + 8 * q + 4 * h + e;
+          const float v = (s_par[co] != 0.0f) ? vmx : vmn;
+          const uint32_t off = (((uint32_t)co * PP + win_off) << 2) | win_bad;
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v),
+                                                o_rsrc, off, 0, 0);
         }
     }
   };
@@ -560,7 +581,9 @@ __global__ void __launch_bounds__(G::NTHR)
 
     const X3_LDS float* xs =
         cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
-    const X3_LDS float* ws = cur + G::XBUF + l32 * G::WP + h * 9;
+    const X3_LDS float* ws =
+        (G::RESW ? (const X3_LDS float*)ldsw : cur + G::XBUF) + l32 * G::WP +
+        h * 9;
     // Software pipeline over the k-steps of the chunk: step s issues the LDS
     // fragment reads of step s+1, its share of the next item's staging
     // loads, then its MFMAs; a scheduling fence keeps that order, so each
@@ -616,6 +639,12 @@ __global__ void __launch_bounds__(G::NTHR)
     const Lim l0 = lim_of(item_of(0));
 #pragma unroll
     for (int i = 0; i < NB_W; ++i) issue(l0, (X3_LDS float*)lds0, i, 0);
+    if constexpr (G::RESW) {
+      // the resident weight tile, once (K is a single chunk: ci0 = 0)
+#pragma unroll
+      for (int i = G::NBI; i < G::NBI + G::NBW; ++i)
+        issue(l0, (X3_LDS float*)lds0, i, 0);
+    }
   }
 #pragma unroll 1
   for (int item = 0; item < nitems; item += 2) {

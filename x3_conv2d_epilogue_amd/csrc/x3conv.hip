@@ -96,7 +96,8 @@ x3_status run_conv(x3::ConvArgs a, hipStream_t st) {
   a.n_ct = (a.Wo + G::TWC - 1) / G::TWC;
   const int64_t ntiles = (int64_t)a.B * a.n_rt * a.n_ct;
   const int64_t nchunk = (a.Cin + G::CC - 1) / G::CC;
-  const int cus = num_cus();
+  // one workgroup per CU resident (two for the 4-wave configurations)
+  const int cus = num_cus() * (G::NWAVE == 4 ? 2 : 1);
   const int64_t grid = ntiles < cus ? ntiles : cus;
   if (ntiles >= (1ll << 31) || (ntiles / grid + 1) * nchunk >= (1ll << 31))
     return fail(X3_EUNSUPPORTED, "problem too large for 32-bit tile counters");
@@ -165,19 +166,44 @@ x3::ConvArgs base_args(const float* x, const float* w, const float* b,
   return a;
 }
 
-// GroupNorm path geometry (Cout = 64 tiles of the dispatch64 table).
+// GroupNorm path geometry.  With Cin <= 8 (one K chunk) the weight tile is
+// resident and two 4-wave workgroups share a CU; otherwise the 8-wave
+// tiles of the Cout = 64 table.  Both have 4-row wave tiles (one row of
+// pooling windows).
 struct GnGeo {
   int th, twc, nwave;
 };
-GnGeo gn_geo(int Wo) {
+GnGeo gn_geo(int Wo, int Cin) {
+  if (Cin <= 8) {
+    if (Wo > 64) return {4, 128, 4};
+    if (Wo > 32) return {8, 64, 4};
+    return {16, 32, 4};
+  }
   if (Wo > 128) return {4, 256, 8};
   if (Wo > 64) return {8, 128, 8};
   if (Wo > 32) return {16, 64, 8};
   return {32, 32, 8};
 }
-int gn_pps(int Ho, int Wo) {  // partial slots per (sample, group)
-  const GnGeo g = gn_geo(Wo);
+int gn_pps(int Ho, int Wo, int Cin) {  // partial slots per (sample, group)
+  const GnGeo g = gn_geo(Wo, Cin);
   return ((Ho + g.th - 1) / g.th) * ((Wo + g.twc - 1) / g.twc) * g.nwave;
+}
+
+template <bool X4>
+x3_status dispatch_gn_(const x3::ConvArgs& a, hipStream_t st) {
+  if (a.Cin <= 8) {
+    if (a.Wo > 64)
+      return run_conv<x3::Geo<2, 8, 4, 4, 4, X4, true>, x3::EPI_GN_POOL>(a, st);
+    if (a.Wo > 32)
+      return run_conv<x3::Geo<2, 8, 8, 2, 4, X4, true>, x3::EPI_GN_POOL>(a, st);
+    return run_conv<x3::Geo<2, 8, 16, 1, 4, X4, true>, x3::EPI_GN_POOL>(a, st);
+  }
+  return dispatch64_<x3::EPI_GN_POOL, X4>(a, st);
+}
+
+x3_status dispatch_gn(const x3::ConvArgs& a, hipStream_t st) {
+  return rows_aligned16(a) ? dispatch_gn_<true>(a, st)
+                           : dispatch_gn_<false>(a, st);
 }
 
 }  // namespace
@@ -267,6 +293,12 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
     return fail(X3_EUNSUPPORTED, "pool_k=%d not compiled in (4)", pool_k);
   if ((uint64_t)Cin * H * W * 4 >= (1ull << 31))
     return fail(X3_EUNSUPPORTED, "one sample of x must be smaller than 2 GiB");
+  const uint64_t P = (uint64_t)((H - 2 - pool_k) / pool_k + 1) *
+                     ((W - 2 - pool_k) / pool_k + 1);
+  if ((uint64_t)Cout * P * 4 >= (1ull << 31) ||
+      (uint64_t)groups * gn_pps(H - 2, W - 2, Cin) * 16 >= (1ull << 31))
+    return fail(X3_EUNSUPPORTED,
+                "one sample of out or of the workspace must be < 2 GiB");
   s = Shape{B, Cin, H, W, Cout, H - 2, W - 2};
   return X3_OK;
 }
@@ -280,7 +312,7 @@ X3_API size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W,
   const x3_status rc = check_gn(B, Cin, H, W, Cout, groups, pool_k, s);
   __builtin_memcpy(g_err, saved, sizeof(g_err));
   if (rc != X3_OK) return 0;
-  return (size_t)B * groups * gn_pps(s.Ho, s.Wo) * sizeof(float4);
+  return (size_t)B * groups * gn_pps(s.Ho, s.Wo, s.Cin) * sizeof(float4);
 }
 
 X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
@@ -300,7 +332,7 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   if (!std::isfinite(lo) || !std::isfinite(hi) || lo > hi)
     return fail(X3_EINVAL, "clamp bounds must be finite with lo <= hi");
   if (B == 0) return X3_OK;
-  const size_t need = (size_t)B * groups * gn_pps(s.Ho, s.Wo) * sizeof(float4);
+  const size_t need = (size_t)B * groups * gn_pps(s.Ho, s.Wo, s.Cin) * sizeof(float4);
   if (!workspace || workspace_bytes < need)
     return fail(X3_EWORKSPACE, "workspace of %zu bytes needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -326,7 +358,7 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   a.Ph = Ph;
   a.Pw = Pw;
   a.groups = groups;
-  rc = dispatch64<x3::EPI_GN_POOL>(a, st);
+  rc = dispatch_gn(a, st);
   if (rc != X3_OK) return rc;
 
   x3::GnFinArgs f{};
@@ -337,7 +369,7 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   f.out = out;
   f.groups = groups;
   f.cpg = Cout / groups;
-  f.pps = gn_pps(s.Ho, s.Wo);
+  f.pps = gn_pps(s.Ho, s.Wo, s.Cin);
   f.plane = Ph * Pw;
   f.eps = eps;
   f.lo = lo;
