@@ -405,6 +405,8 @@ __global__ void __launch_bounds__(G::NTHR)
       static_assert(G::NW % 2 == 0, "lane halves split the N-tiles");
       constexpr int HN = G::NW / 2;
       const bool use_max = (EPI == EPI_SCALE_MIN) && !(a.s0 >= 0.0f);
+      const __amdgpu_buffer_rsrc_t o_rsrc =
+          make_rsrc(a.out + (size_t)n * a.Ho * a.Wo, (uint32_t)(a.Ho * a.Wo * 4));
       float m[G::NW];
 #pragma unroll
       for (int j = 0; j < G::NW; ++j) {
@@ -427,24 +429,42 @@ __global__ void __launch_bounds__(G::NTHR)
           y = tanhf(tanhf(v));
         else
           y = a.s0 * v;
-        if (col_ok && r < a.Ho) a.out[((size_t)n * a.Ho + r) * a.Wo + c] = y;
+        // bounded store into this sample's output plane; bit 31 drops it
+        const uint32_t off = ((uint32_t)(r * a.Wo + c) << 2) |
+                             ((uint32_t)!(col_ok && r < a.Ho) << 31);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y),
+                                              o_rsrc, off, 0, 0);
       }
     } else if constexpr (EPI == EPI_MUL_LRELU_GELU) {
       const float slope = a.s0;
+      // bounded stores into this sample's [Cout][Ho][Wo] block; an offset
+      // with bit 31 set (pixel outside the output) is dropped
+      const int HoWo = a.Ho * a.Wo;
+      const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
+          a.out + (size_t)n * G::COUT * HoWo, (uint32_t)(G::COUT * HoWo * 4));
+      uint32_t pix_off[G::NW], drop[G::NW];
+#pragma unroll
+      for (int j = 0; j < G::NW; ++j) {
+        const int r = r_base + j;
+        pix_off[j] = (uint32_t)(r * a.Wo + c);
+        drop[j] = (uint32_t)!(col_ok && r < a.Ho) << 31;
+      }
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int co = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
           const float mv = s_par[co];
-          float* orow = a.out + (((size_t)n * G::COUT + co) * a.Ho) * a.Wo + c;
 #pragma unroll
           for (int j = 0; j < G::NW; ++j) {
             float v = acc[mt][j][i] * mv;
             v = (v >= 0.0f) ? v : slope * v;
             const float y = 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
-            const int r = r_base + j;
-            if (col_ok && r < a.Ho) orow[(size_t)r * a.Wo] = y;
+            // (OR, not add: nothing can clear the drop bit)
+            const uint32_t off =
+                (((uint32_t)co * HoWo + pix_off[j]) << 2) | drop[j];
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(uint32_t, y), o_rsrc, off, 0, 0);
           }
         }
     } else {  // EPI_GN_POOL: requires NW == 4, Cout/groups == 4, pool 4

@@ -237,6 +237,8 @@ X3_API x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
   x3_status rc = check_common(x, w, b, out, B, Cin, H, W, Cout, s);
   if (rc != X3_OK) return rc;
   if (!mult) return fail(X3_EINVAL, "null multiplier pointer");
+  if ((uint64_t)Cout * (H - 2) * (W - 2) * 4 >= (1ull << 31))
+    return fail(X3_EUNSUPPORTED, "one sample of out must be smaller than 2 GiB");
   if (!std::isfinite(neg_slope))
     return fail(X3_EINVAL, "neg_slope must be finite");
   if (B == 0) return X3_OK;
