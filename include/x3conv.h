@@ -38,9 +38,10 @@
  *   prints; the return value is an x3_status and x3_last_error() gives a
  *   thread-local detail string for the last failure on the calling thread.
  * - `out` must not overlap any input.  Inputs are never written.
- * - Supported: Cout in {64, 128}; 3 <= H, W; Cin >= 1; each sample of x
- *   smaller than 2 GiB; every other positive shape works (ragged tiles are
- *   masked inside the kernels).  Anything else returns X3_EUNSUPPORTED.
+ * - Supported: 1 <= Cout <= 1024; 3 <= H, W; Cin >= 1; each sample of x
+ *   smaller than 2 GiB; every other positive shape works (ragged tiles and
+ *   channel counts are masked inside the kernels).  Anything else returns
+ *   X3_EUNSUPPORTED.
  * - B == 0 is a valid empty call: nothing is enqueued and X3_OK is returned.
  */
 #ifndef X3CONV_H
@@ -57,7 +58,7 @@ enum {
   X3_OK = 0,            /* enqueued (or nothing to do) */
   X3_EINVAL = 1,        /* null pointer, negative size, non-finite scalar */
   X3_ESHAPE = 2,        /* shape cannot produce an output (H or W < 3, ...) */
-  X3_EUNSUPPORTED = 3,  /* valid but not compiled in (e.g. Cout not 64/128) */
+  X3_EUNSUPPORTED = 3,  /* valid but not compiled in (e.g. Cout > 1024) */
   X3_EWORKSPACE = 4,    /* workspace missing or too small */
   X3_EHIP = 5           /* the HIP runtime reported an error at launch */
 };
@@ -72,7 +73,10 @@ x3_status x3_conv3x3_min_tanh2_f32(const float* x, const float* w,
  * v = (v >= 0) ? v : neg_slope * v  (LeakyReLU; the page uses 0.01);
  * out[n,co,h,w] = 0.5 * v * (1 + erf(v / sqrt(2)))  (exact GELU).
  * mult: [Cout] (the page's [Cout,1,1] parameter).  out: [B][Cout][Ho][Wo].
- * neg_slope must be finite (else X3_EINVAL). */
+ * neg_slope must be finite (else X3_EINVAL).  One sample of out, with Cout
+ * rounded up to the kernel's channel block (64, or 128 when Cout > 64 and
+ * that rounds no higher), must be smaller than 2 GiB (else
+ * X3_EUNSUPPORTED). */
 x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
                                         const float* b, const float* mult,
                                         float neg_slope, float* out, int B,
@@ -107,7 +111,8 @@ size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W, int Cout,
  * overwritten, and two calls sharing one workspace must be ordered on one
  * stream.  Two kernels are enqueued on `stream` (statistics + window
  * extrema, then finalize); `out` holds intermediate values between them.
- * Supported: Cout / groups == 4, pool_k == 4 (else X3_EUNSUPPORTED);
+ * Supported: Cout / groups == 4 (any Cout up to 1024 that is a multiple of
+ * 4), pool_k == 4 (else X3_EUNSUPPORTED);
  * eps > 0 and finite lo <= hi (else X3_EINVAL); Ho, Wo >= pool_k (else
  * X3_ESHAPE). */
 x3_status x3_conv3x3_gn_scale_pool_clamp_f32(

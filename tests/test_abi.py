@@ -71,8 +71,8 @@ def test_min_tanh2_validation(lib):
     assert _min(lib, X, W_, B_, O, 2, 0, 32, 32, 64, s) == EINVAL
     assert _min(lib, X, W_, B_, O, 2, 16, 2, 32, 64, s) == ESHAPE
     assert _min(lib, X, W_, B_, O, 2, 16, 32, 2, 64, s) == ESHAPE
-    assert _min(lib, X, W_, B_, O, 2, 16, 32, 32, 48, s) == EUNSUP
-    assert b"Cout=48" in lib.x3_last_error()
+    assert _min(lib, X, W_, B_, O, 2, 16, 32, 32, 1025, s) == EUNSUP
+    assert b"Cout=1025" in lib.x3_last_error()
     assert _min(lib, None, W_, B_, O, 2, 16, 32, 32, 64, s) == EINVAL
     assert _min(lib, X, None, B_, O, 2, 16, 32, 32, 64, s) == EINVAL
     assert _min(lib, X, W_, None, O, 2, 16, 32, 32, 64, s) == EINVAL
@@ -92,7 +92,9 @@ def test_mul_lrelu_gelu_validation(lib):
     assert f(X, W_, B_, None, 0.01, O, 2, 16, 32, 32, 64, s) == EINVAL
     assert f(X, W_, B_, M, float("nan"), O, 2, 16, 32, 32, 64, s) == EINVAL
     assert f(X, W_, B_, M, float("inf"), O, 2, 16, 32, 32, 64, s) == EINVAL
-    assert f(X, W_, B_, M, 0.01, O, 2, 16, 32, 32, 96, s) == EUNSUP
+    assert f(X, W_, B_, M, 0.01, O, 2, 16, 32, 32, 1100, s) == EUNSUP
+    # a sample of out (padded to whole 128-channel blocks) of 2 GiB or more
+    assert f(X, W_, B_, M, 0.01, O, 1, 4, 4098, 1026, 127, s) == EUNSUP
     assert f(X, W_, B_, M, 0.01, M, 2, 16, 32, 32, 64, s) == EINVAL  # out == mult
     assert f(None, W_, B_, M, 0.01, None, 0, 16, 32, 32, 64, s) == OK
 
@@ -102,21 +104,27 @@ def test_scale_min_validation(lib):
     s = P(0)
     assert f(X, W_, B_, float("nan"), O, 2, 64, 32, 32, 128, s) == EINVAL
     assert f(X, W_, B_, 2.0, O, 2, 64, 1, 32, 128, s) == ESHAPE
-    assert f(X, W_, B_, 2.0, O, 2, 64, 32, 32, 256, s) == EUNSUP
+    assert f(X, W_, B_, 2.0, O, 2, 64, 32, 32, 2000, s) == EUNSUP
     assert f(X, W_, B_, 2.0, B_, 2, 64, 32, 32, 128, s) == EINVAL  # out == bias
 
 
 def test_gn_workspace_bytes(lib):
     f = lib.x3_conv3x3_gn_workspace_bytes
-    # [128,8,128,128] -> conv 126x126, tiles of 8 rows x 128 columns, 8 waves:
-    # 16 row tiles * 1 column tile * 8 = 128 partial slots per (n, g) of 16 B
+    # [128,8,128,128] -> conv 126x126; Cin <= 8 and Cout <= 64: tiles of 4 rows
+    # x 128 columns, 4 waves: 32 row tiles * 1 column tile * 4 = 128 partial
+    # slots per (n, g) of 16 B
     assert f(128, 8, 128, 128, 64, 16, 4) == 128 * 16 * 128 * 16
+    # Cout 128: 64-channel blocks, tiles of 8 rows x 128 columns, 8 waves:
+    # 16 * 1 * 8 = 128 slots
+    assert f(2, 8, 128, 128, 128, 32, 4) == 2 * 32 * 128 * 16
+    # Cin 16 (two K chunks): the same 8-wave tiles
+    assert f(2, 16, 128, 128, 64, 16, 4) == 2 * 16 * 128 * 16
     assert f(0, 8, 128, 128, 64, 16, 4) == 0
     assert f(2, 8, 128, 128, 64, 15, 4) == 0   # 64 % 15
     assert f(2, 8, 128, 128, 64, 8, 4) == 0    # 8 channels per group: not compiled
     assert f(2, 8, 128, 128, 64, 16, 3) == 0   # pool 3: not compiled
     assert f(2, 8, 5, 5, 64, 16, 4) == 0       # 3x3 conv output < pool window
-    assert f(2, 8, 128, 128, 128, 32, 4) == 0  # Cout 128: not compiled for GN
+    assert f(2, 8, 128, 128, 1028, 257, 4) == 0  # Cout above 1024
 
 
 def test_gn_validation(lib):
@@ -141,7 +149,9 @@ def test_gn_validation(lib):
     assert call(H=5) == ESHAPE
     assert call(groups=8) == EUNSUP
     assert call(k=2) == EUNSUP
-    assert call(Cout=128, groups=32) == EUNSUP
+    assert call(Cout=1028, groups=257) == EUNSUP
+    # Cout 128 is supported, but needs a workspace for 32 groups
+    assert call(Cout=128, groups=32) == EWS
     assert call(eps=0.0) == EINVAL
     assert call(eps=float("nan")) == EINVAL
     assert call(lo=1.0, hi=0.0) == EINVAL

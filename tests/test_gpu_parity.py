@@ -211,10 +211,79 @@ def test_edge_empty_batch():
 
 
 def test_unsupported_cout_raises():
-    d = to_dev(random_case("min_tanh2", 1, 4, 8, 8, 32, seed=704))
+    d = to_dev(random_case("min_tanh2", 1, 4, 8, 8, 1025, seed=704))
     with pytest.raises(x3.X3Error) as e:
         x3.conv3x3_min_tanh2(d["x"], d["weight"], d["bias"])
     assert e.value.status_name == "X3_EUNSUPPORTED"
+
+
+# Channel counts against the kernels' channel blocks (64 channels per pass,
+# or 128 when that pads no more): a partial single block (1, 17, 40), a
+# partial 128-block (96, 100), three 64-blocks with a partial last one
+# (160), two 128-blocks with a partial last one (200), whole blocks (256),
+# five 64-blocks (320) and the largest supported count (1024 = 8 passes).
+COUTS = [1, 17, 40, 96, 100, 160, 200, 256, 320]
+SHAPES_C = [  # (B, Cin, H, W)
+    (2, 8, 21, 37),     # Wo=35: 2 strips, ragged
+    (1, 11, 12, 131),   # Wo=129: 8-strip tile, two K chunks
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_C)
+@pytest.mark.parametrize("Cout", COUTS)
+def test_any_cout_scale_min_integer_bit_exact(shape, Cout):
+    B, Cin, H, W = shape
+    say(f"scale_min int-exact {shape} Cout={Cout}")
+    d = random_case("scale_min", B, Cin, H, W, Cout, seed=800 + Cout, dist="int")
+    for scale in (2.0, -1.0):
+        got = run_op("scale_min", d, scale=scale)
+        ref = run_oracle("scale_min", d, scale=scale)
+        assert np.array_equal(got.astype(np.float64), ref), \
+            f"scale {scale}: max diff {np.abs(got - ref).max()}"
+
+
+@pytest.mark.parametrize("Cout", COUTS)
+def test_any_cout_min_tanh2(Cout):
+    shape = SHAPES_C[Cout % 2]
+    say(f"min_tanh2 {shape} Cout={Cout}")
+    d = random_case("min_tanh2", *shape, Cout, seed=900 + Cout)
+    assert_close(run_op("min_tanh2", d), run_oracle("min_tanh2", d), what=f"Cout={Cout}")
+
+
+@pytest.mark.parametrize("Cout", COUTS)
+def test_any_cout_mul_lrelu_gelu(Cout):
+    shape = SHAPES_C[(Cout + 1) % 2]
+    say(f"mul_lrelu_gelu {shape} Cout={Cout}")
+    d = random_case("mul_lrelu_gelu", *shape, Cout, seed=1000 + Cout)
+    assert_close(run_op("mul_lrelu_gelu", d), run_oracle("mul_lrelu_gelu", d),
+                 what=f"Cout={Cout}")
+
+
+def test_max_cout_1024():
+    say("Cout=1024, all three single-pass epilogues")
+    d = random_case("min_tanh2", 1, 4, 10, 40, 1024, seed=1100)
+    assert_close(run_op("min_tanh2", d), run_oracle("min_tanh2", d), what="min_tanh2 1024")
+    d = random_case("mul_lrelu_gelu", 1, 4, 10, 40, 1024, seed=1101)
+    assert_close(run_op("mul_lrelu_gelu", d), run_oracle("mul_lrelu_gelu", d),
+                 what="gelu 1024")
+    d = random_case("scale_min", 1, 4, 10, 40, 1024, seed=1102, dist="int")
+    got = run_op("scale_min", d, scale=-1.0)
+    assert np.array_equal(got.astype(np.float64), run_oracle("scale_min", d, scale=-1.0))
+
+
+# GroupNorm with 4 channels per group and other channel counts: a mostly
+# padded block (4), a partial block (36), the resident-weight limit (64),
+# several 64-channel passes with and without a partial one (68, 128, 200).
+@pytest.mark.parametrize("Cout", [4, 36, 68, 128, 200])
+@pytest.mark.parametrize("shape", [(2, 8, 34, 34), (1, 16, 18, 131)])
+def test_any_cout_gn_pool(Cout, shape):
+    B, Cin, H, W = shape
+    say(f"gn_pool {shape} Cout={Cout}")
+    d = random_case("gn_scale_pool_clamp", B, Cin, H, W, Cout, seed=1200 + Cout)
+    d["gamma"][::3] *= -1.0
+    kw = dict(groups=Cout // 4, lo=-50.0, hi=50.0)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw),
+                 run_oracle("gn_scale_pool_clamp", d, **kw), what=f"Cout={Cout}")
 
 
 def test_non_default_stream_and_determinism():

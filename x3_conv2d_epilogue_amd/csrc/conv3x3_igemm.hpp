@@ -13,9 +13,13 @@
 //
 // Work decomposition
 //   * A workgroup tile is TH output rows x TWC = 32*NCT output columns of one
-//     sample, and ALL output channels (Cout = 32*MT), so channel reductions
-//     (the min epilogues) never leave the workgroup -- they never leave the
-//     wavefront, in fact.
+//     sample, and ALL output channels, so channel reductions (the min
+//     epilogues) never leave the workgroup -- they never leave the
+//     wavefront, in fact.  The channels are covered by ncb passes over
+//     channel blocks of COUT = 32*MT; the last block is padded with zero
+//     weight rows (and, for the channel-min epilogues, with a bias of
+//     +-infinity, so a padded channel never wins).  The min epilogues carry
+//     a running per-pixel extremum in registers from pass to pass.
 //   * The tile is split into 32x32 MFMA blocks: M = 32 channels, N = 32
 //     consecutive pixels of one output row.  Each of the NWAVE wavefronts
 //     owns all MT channel blocks for NW pixel blocks ("N-tiles") that sit in
@@ -78,15 +82,19 @@ struct ConvArgs {
   int n_rt, n_ct;   // row tiles, column tiles per sample
   int ntiles;       // B * n_rt * n_ct
   int nchunk;       // ceil(Cin / CC)
+  int ncb;          // channel-block passes per tile: ceil(Cout / COUT)
   int Ph, Pw;       // pooled output size (EPI_GN_POOL)
   int groups;       // GroupNorm groups (EPI_GN_POOL)
 };
+
+// Largest Cout: per-channel constants of all channel blocks live in LDS.
+constexpr int kMaxCout = 1024;
 
 // Compile-time geometry of one kernel configuration.
 template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_, bool X4_,
           bool RESW_ = false>
 struct Geo {
-  static constexpr int MT = MT_;          // 32-channel blocks (Cout = 32*MT)
+  static constexpr int MT = MT_;          // 32-channel MFMA blocks per pass
   static constexpr int CC = CC_;          // input channels per K chunk
   static constexpr int TH = TH_;          // output rows per tile
   static constexpr int NCT = NCT_;        // 32-column strips per tile
@@ -98,7 +106,7 @@ struct Geo {
   // when K fits one chunk, Cin <= CC); items then stage the input only.
   static constexpr bool RESW = RESW_;
   static constexpr int NTHR = NWAVE * 64;
-  static constexpr int COUT = 32 * MT;
+  static constexpr int COUT = 32 * MT;    // channels per pass
   static constexpr int TWC = 32 * NCT;    // output columns per tile
   static constexpr int XROWS = TH + 2;    // input rows per tile (halo)
   static constexpr int XCOLS = TWC + 2;   // input columns per tile (halo)
@@ -134,7 +142,7 @@ struct Geo {
   static_assert(XBUF % 256 == 0 && WBUF % 64 == 0, "whole staging blocks");
   static_assert(NTILE_N % NWAVE == 0, "N-tiles must split evenly over waves");
   static_assert(TH % NW == 0, "a wave's N-tiles must lie in one strip");
-  static_assert(LDS_DWORDS * 4 + 2 * COUT * 4 <= 160 * 1024,
+  static_assert(LDS_DWORDS * 4 + 2 * kMaxCout * 4 <= 160 * 1024,
                 "LDS budget exceeded");
   static_assert(XBUF * 4 < 65536 && WBUF * 4 < 65536,
                 "ds_read immediates are 16-bit");
@@ -244,13 +252,14 @@ __global__ void __launch_bounds__(G::NTHR)
   __shared__ float lds0[G::STAGE];
   __shared__ float lds1[G::STAGE];
   __shared__ float ldsw[G::RESW ? G::WBUF : 1];  // resident weight tile
-  // Per-channel constants, loaded once: bias, and the epilogue's channel
-  // parameter (multiplier, or for the pooling path the direction flag
-  // 1 = keep the window maximum, 0 = keep the minimum).  Reading them from
-  // LDS keeps global loads out of the main loop, whose vmcnt waits would
-  // otherwise also wait for the next stage's prefetch.
-  __shared__ float s_bias[G::COUT];
-  __shared__ float s_par[G::COUT];
+  // Per-channel constants of all ncb*COUT (padded) channels, loaded once:
+  // bias, and the epilogue's channel parameter (multiplier, or for the
+  // pooling path the direction flag 1 = keep the window maximum, 0 = keep
+  // the minimum).  Reading them from LDS keeps global loads out of the main
+  // loop, whose vmcnt waits would otherwise also wait for the next stage's
+  // prefetch.
+  __shared__ float s_bias[kMaxCout];
+  __shared__ float s_par[kMaxCout];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -266,7 +275,7 @@ __global__ void __launch_bounds__(G::NTHR)
   int vb = blockIdx.x;
   if ((G_ & 7) == 0) vb = (blockIdx.x & 7) * (G_ >> 3) + (blockIdx.x >> 3);
   const int my_tiles = (a.ntiles > vb) ? (a.ntiles - vb + G_ - 1) / G_ : 0;
-  const int nitems = my_tiles * a.nchunk;
+  const int nitems = my_tiles * a.ncb * a.nchunk;
 
   const uint32_t x_sample = (uint32_t)a.Cin * a.H * a.W;  // floats
   const __amdgpu_buffer_rsrc_t w_rsrc =
@@ -276,15 +285,32 @@ __global__ void __launch_bounds__(G::NTHR)
   // The stage is filled in blocks, one direct-to-LDS load per block and
   // wave (lane l writes piece l of the block).  Wave w owns input blocks
   // w + NWAVE*i (i < NBI) and weight blocks w + NWAVE*i (i < NBW).
-  // Elements that must be zero (rows past H, channels >= Cin, weight-row
-  // padding) are read from an offset past the buffer end and land as 0.
-  struct Item {
-    int n, r0, c0, ci0;
+  // Elements that must be zero (rows past H, input channels >= Cin, weight
+  // columns past the chunk's K) are read from an offset past the buffer end
+  // and land as 0; so do the weight rows of padded output channels, whose
+  // offsets lie past the end of the weight tensor by construction.
+  //
+  // Items run tile by tile; inside a tile, channel block by channel block;
+  // inside a block, K chunk by K chunk.  A position in that walk is
+  // advanced incrementally (no integer division per item).
+  struct Pos {
+    int tl, cb, chunk;  // local tile index, channel block, K chunk
   };
-  auto item_of = [&](int item) X3_INLINE {
-    const int tl = item / a.nchunk;
-    const int chunk = item - tl * a.nchunk;
-    const int t = vb + tl * G_;
+  auto advance = [&](const Pos& p) X3_INLINE {
+    const bool end_k = p.chunk + 1 == a.nchunk;
+    const bool end_c = end_k && (p.cb + 1 == a.ncb);
+    Pos q;
+    q.chunk = end_k ? 0 : p.chunk + 1;
+    q.cb = end_c ? 0 : (end_k ? p.cb + 1 : p.cb);
+    q.tl = end_c ? p.tl + 1 : p.tl;
+    return q;
+  };
+  struct Item {
+    int n, r0, c0, ci0, co0;
+  };
+  auto item_of = [&](const Pos& p) X3_INLINE {
+    const int t = vb + p.tl * G_;
+    const int chunk = p.chunk, cb = p.cb;
     const int ct = t % a.n_ct;
     const int rt = (t / a.n_ct) % a.n_rt;
     Item it;
@@ -292,6 +318,7 @@ __global__ void __launch_bounds__(G::NTHR)
     it.r0 = rt * G::TH;
     it.c0 = ct * G::TWC;
     it.ci0 = chunk * G::CC;
+    it.co0 = cb * G::COUT;
     return it;
   };
   // Uniform per-item limits, computed once per item.
@@ -302,8 +329,9 @@ __global__ void __launch_bounds__(G::NTHR)
     int row_lim;   // local rows < row_lim are real
     int col_lim;   // local columns < col_lim are needed and real
     int kk_lim;    // weight columns < kk_lim are real
-    int wbase;     // element offset of input channel ci0 in a weight row
+    int wbase;     // element offset of (co0, ci0) in the weight tensor
   };
+  const int HW = a.H * a.W, CinK = a.Cin * 9;
   auto lim_of = [&](const Item& it) X3_INLINE {
     Lim l;
     l.xr = make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
@@ -315,10 +343,9 @@ __global__ void __launch_bounds__(G::NTHR)
     l.col_lim = cl < G::XCOLS ? cl : G::XCOLS;
     const int kl = 9 * (a.Cin - it.ci0);
     l.kk_lim = kl < G::KC ? kl : G::KC;
-    l.wbase = it.ci0 * 9;
+    l.wbase = it.co0 * CinK + it.ci0 * 9;
     return l;
   };
-  const int HW = a.H * a.W, CinK = a.Cin * 9;
   // Wave-local block i (compile-time) of the stage at `sbase`.  `zz` is an
   // opaque per-item zero: it keeps the lane-dependent address arithmetic
   // from being hoisted out of the item loop (which would pin one register
@@ -359,7 +386,7 @@ __global__ void __launch_bounds__(G::NTHR)
       const uint32_t q = (uint32_t)(blk * 64 + lane);
       const uint32_t co = q / G::WP;
       const uint32_t kk = q - co * G::WP;
-      const bool ok = (kk < (uint32_t)l.kk_lim);
+      const bool ok = kk < (uint32_t)l.kk_lim;
       const uint32_t off =
           ((co * (uint32_t)CinK + (uint32_t)l.wbase + kk) << 2) |
           ((uint32_t)!ok << 31);
@@ -376,20 +403,39 @@ __global__ void __launch_bounds__(G::NTHR)
 
   const WaveMap<G> wm(wave);
 
-  for (int co = tid; co < G::COUT; co += G::NTHR) {
-    s_bias[co] = a.b[co];
-    float pv = 0.0f;
-    if constexpr (EPI == EPI_MUL_LRELU_GELU) pv = a.v0[co];
-    if constexpr (EPI == EPI_GN_POOL)
-      pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : 0.0f;
+  // Padded channels (co >= Cout) get the bias that loses every channel
+  // comparison: +inf for a minimum, -inf for a maximum (scale_min with a
+  // negative scale takes the maximum before scaling); their weight rows are
+  // zero, so the accumulator stays at that bias.  Other epilogues never
+  // store padded channels.
+  float pad = 0.0f;
+  if constexpr (EPI == EPI_MIN_TANH2) pad = __builtin_inff();
+  if constexpr (EPI == EPI_SCALE_MIN)
+    pad = (a.s0 >= 0.0f) ? __builtin_inff() : -__builtin_inff();
+  for (int co = tid; co < a.ncb * G::COUT; co += G::NTHR) {
+    const bool real = co < a.Cout;
+    float bv = pad, pv = 0.0f;
+    if (real) {
+      bv = a.b[co];
+      if constexpr (EPI == EPI_MUL_LRELU_GELU) pv = a.v0[co];
+      if constexpr (EPI == EPI_GN_POOL)
+        pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : 0.0f;
+    }
+    s_bias[co] = bv;
     s_par[co] = pv;
   }
   // (made visible by the barrier at the top of the first item)
 
   f32x16 acc[G::MT][G::NW];
+  // running channel extremum of the min epilogues, per N-tile, carried from
+  // one channel-block pass of a tile to the next
+  float run[G::NW];
+#pragma unroll
+  for (int j = 0; j < G::NW; ++j) run[j] = 0.0f;
 
-  auto epilogue = [&](int t) X3_INLINE {
-    // ---- epilogue for tile t --------------------------------------------------
+  auto epilogue = [&](int t, int cb) X3_INLINE {
+    // ---- epilogue for channel block cb of tile t ------------------------------
+    const int co0 = cb * G::COUT;
     const int ct = t % a.n_ct;
     const int rt = (t / a.n_ct) % a.n_rt;
     const int n = t / (a.n_ct * a.n_rt);
@@ -418,6 +464,16 @@ __global__ void __launch_bounds__(G::NTHR)
             v = use_max ? fmaxf(v, acc[mt][j][i]) : fminf(v, acc[mt][j][i]);
         m[j] = v;
       }
+      if (a.ncb > 1) {  // (uniform) fold in the earlier blocks' extremum
+        const bool first = cb == 0;
+#pragma unroll
+        for (int j = 0; j < G::NW; ++j) {
+          const float r = use_max ? fmaxf(m[j], run[j]) : fminf(m[j], run[j]);
+          m[j] = first ? m[j] : r;
+          run[j] = m[j];
+        }
+        if (cb != a.ncb - 1) return;  // more channel blocks to come
+      }
 #pragma unroll
       for (int jj = 0; jj < HN; ++jj) {
         const float keep = h ? m[jj + HN] : m[jj];
@@ -439,9 +495,10 @@ __global__ void __launch_bounds__(G::NTHR)
       const float slope = a.s0;
       // bounded stores into this sample's [Cout][Ho][Wo] block; an offset
       // with bit 31 set (pixel outside the output) is dropped
+      // (padded channels land past the end of the block and are dropped)
       const int HoWo = a.Ho * a.Wo;
       const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
-          a.out + (size_t)n * G::COUT * HoWo, (uint32_t)(G::COUT * HoWo * 4));
+          a.out + (size_t)n * a.Cout * HoWo, (uint32_t)(a.Cout * HoWo * 4));
       uint32_t pix_off[G::NW], drop[G::NW];
 #pragma unroll
       for (int j = 0; j < G::NW; ++j) {
@@ -453,7 +510,7 @@ __global__ void __launch_bounds__(G::NTHR)
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int co = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          const int co = co0 + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
           const float mv = s_par[co];
 #pragma unroll
           for (int j = 0; j < G::NW; ++j) {
@@ -475,8 +532,9 @@ __global__ void __launch_bounds__(G::NTHR)
       // epilogue has no exec-masked branches.
       const int PP = a.Ph * a.Pw;
       const int pps = a.n_rt * a.n_ct * G::NWAVE;
+      // (padded channels and groups land past the ends and are dropped)
       const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
-          a.out + (size_t)n * G::COUT * PP, (uint32_t)(G::COUT * PP * 4));
+          a.out + (size_t)n * a.Cout * PP, (uint32_t)(a.Cout * PP * 4));
       const __amdgpu_buffer_rsrc_t p_rsrc =
           make_rsrc(a.part + (size_t)n * a.groups * pps,
                     (uint32_t)(a.groups * pps * 16));
@@ -517,8 +575,8 @@ __global__ void __launch_bounds__(G::NTHR)
           my_m2 = mine ? fmaxf(s2 - s1 * s1 * inv_cnt, 0.0f) : my_m2;
         }
       {
-        // lane (h, l32 = mt*4+q) writes group g = mt*8 + 2q + h
-        const int g = (l32 >> 2) * 8 + 2 * (l32 & 3) + h;
+        // lane (h, l32 = mt*4+q) writes group g = co0/4 + mt*8 + 2q + h
+        const int g = (co0 >> 2) + (l32 >> 2) * 8 + 2 * (l32 & 3) + h;
         const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
         const uint32_t off = ((uint32_t)(g * pps + slot) << 4) |
                              ((uint32_t)(l32 >= G::MT * 4) << 31);
@@ -560,7 +618,7 @@ __global__ void __launch_bounds__(G::NTHR)
           }
           const float vmx = e == 0 ? mx[0] : (e == 1 ? mx[1] : (e == 2 ? mx[2] : mx[3]));
           const float vmn = e == 0 ? mn[0] : (e == 1 ? mn[1] : (e == 2 ? mn[2] : mn[3]));
-          const int co = mt * 32 + 8 * q + 4 * h + e;
+          const int co = co0 + mt * 32 + 8 * q + 4 * h + e;
           const float v = (s_par[co] != 0.0f) ? vmx : vmn;
           const uint32_t off = (((uint32_t)co * PP + win_off) << 2) | win_bad;
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v),
@@ -571,29 +629,36 @@ __global__ void __launch_bounds__(G::NTHR)
 
   // ---- one item: wait for its stage, prefetch the next item into the other
   // stage from inside the MFMA loop, multiply, and finish the tile ----------
-  auto run_item = [&](auto bufc, int item) X3_INLINE {
+  auto run_item = [&](auto bufc, int item, Pos& pos) X3_INLINE {
     constexpr int BUF = decltype(bufc)::value;
     X3_LDS float* cur = BUF ? (X3_LDS float*)lds1 : (X3_LDS float*)lds0;
     X3_LDS float* nxt = BUF ? (X3_LDS float*)lds0 : (X3_LDS float*)lds1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    // the next item, or on the last item this item again (its data are
+    // in bounds; the reload is never used)
     const bool has_next = item + 1 < nitems;
-    const Lim nl = lim_of(item_of(has_next ? item + 1 : item));
+    const Pos np = advance(pos);
+    Pos pp;
+    pp.tl = has_next ? np.tl : pos.tl;
+    pp.cb = has_next ? np.cb : pos.cb;
+    pp.chunk = has_next ? np.chunk : pos.chunk;
+    const Lim nl = lim_of(item_of(pp));
     int zz;
     asm volatile("s_mov_b32 %0, 0" : "=s"(zz));
 
-    const int tl = item / a.nchunk;
-    const int chunk = item - tl * a.nchunk;
-    const int t = vb + tl * G_;
+    const int cb = pos.cb, chunk = pos.chunk;
+    const int t = vb + pos.tl * G_;
 
     if (chunk == 0) {
       // accumulators start at the bias
+      const X3_LDS float* sb = (const X3_LDS float*)s_bias + cb * G::COUT;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float bv = s_bias[mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)];
+          const float bv = sb[mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)];
 #pragma unroll
           for (int j = 0; j < G::NW; ++j) acc[mt][j][i] = bv;
         }
@@ -652,11 +717,16 @@ __global__ void __launch_bounds__(G::NTHR)
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (chunk == a.nchunk - 1) epilogue(t);
+    if (chunk == a.nchunk - 1) epilogue(t, cb);
+    pos = np;
   };
 
+  Pos pos;
+  pos.tl = 0;
+  pos.cb = 0;
+  pos.chunk = 0;
   if (nitems > 0) {
-    const Lim l0 = lim_of(item_of(0));
+    const Lim l0 = lim_of(item_of(pos));
 #pragma unroll
     for (int i = 0; i < NB_W; ++i) issue(l0, (X3_LDS float*)lds0, i, 0);
     if constexpr (G::RESW) {
@@ -668,8 +738,9 @@ __global__ void __launch_bounds__(G::NTHR)
   }
 #pragma unroll 1
   for (int item = 0; item < nitems; item += 2) {
-    run_item(std::integral_constant<int, 0>{}, item);
-    if (item + 1 < nitems) run_item(std::integral_constant<int, 1>{}, item + 1);
+    run_item(std::integral_constant<int, 0>{}, item, pos);
+    if (item + 1 < nitems)
+      run_item(std::integral_constant<int, 1>{}, item + 1, pos);
   }
   // the last item's (unused) prefetch must land before the LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -1,0 +1,117 @@
+// dispatch.hpp -- host-side launch of the fused kernels: the choice of the
+// kernel configuration for a shape, shared by the per-epilogue translation
+// units (epi_*.hip) and the C ABI (x3conv.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "conv3x3_igemm.hpp"
+#include "x3conv.h"
+
+namespace x3i {
+
+// Set the thread's last-error message and return `s` (defined in x3conv.hip).
+x3_status fail(x3_status s, const char* fmt, ...);
+// Compute units of the current device.
+int num_cus();
+
+// Channel-block width of the kernel configurations: MT = 4 (128 channels
+// per pass, 2 N-tiles per wave) when that pads Cout no more than MT = 2
+// (64 channels per pass, 4 N-tiles per wave) does, otherwise MT = 2.
+inline int channel_block_mt(int Cout) {
+  const int p64 = (Cout + 63) / 64 * 64, p128 = (Cout + 127) / 128 * 128;
+  return (Cout > 64 && p128 == p64) ? 4 : 2;
+}
+// Cout rounded up to whole channel blocks of the configuration used.
+inline int padded_cout(int Cout) {
+  const int cb = 32 * channel_block_mt(Cout);
+  return (Cout + cb - 1) / cb * cb;
+}
+
+// Input rows are 16-byte aligned when W % 4 == 0 (x itself comes from the
+// caller's allocator, checked for 16-byte alignment): then the input is
+// staged with 16-byte loads.
+inline bool rows_aligned16(const x3::ConvArgs& a) {
+  return (a.W % 4 == 0) && (((uintptr_t)a.x & 15u) == 0);
+}
+
+template <class G, int EPI>
+x3_status run_conv(x3::ConvArgs a, hipStream_t st) {
+  a.n_rt = (a.Ho + G::TH - 1) / G::TH;
+  a.n_ct = (a.Wo + G::TWC - 1) / G::TWC;
+  const int64_t ntiles = (int64_t)a.B * a.n_rt * a.n_ct;
+  const int64_t nchunk = (a.Cin + G::CC - 1) / G::CC;
+  const int64_t ncb = (a.Cout + G::COUT - 1) / G::COUT;
+  if (ncb * G::COUT > x3::kMaxCout)
+    return fail(X3_EUNSUPPORTED, "Cout=%d exceeds %d", a.Cout, x3::kMaxCout);
+  // weight rows of padded channels are addressed past the end of w: those
+  // 32-bit byte offsets must not wrap
+  if (ncb * G::COUT * a.Cin * 9 * 4 >= (1ll << 31))
+    return fail(X3_EUNSUPPORTED, "weights padded to whole channel blocks "
+                "must stay below 2 GiB");
+  // a resident weight tile needs a single (channel block, K chunk) pair
+  if (G::RESW && (ncb != 1 || nchunk != 1))
+    return fail(X3_EUNSUPPORTED, "resident-weight configuration misapplied");
+  // one workgroup per CU resident (two for the 4-wave configurations)
+  const int cus = num_cus() * (G::NWAVE == 4 ? 2 : 1);
+  const int64_t grid = ntiles < cus ? ntiles : cus;
+  if (ntiles >= (1ll << 31) || (ntiles / grid + 1) * ncb * nchunk >= (1ll << 31))
+    return fail(X3_EUNSUPPORTED, "problem too large for 32-bit item counters");
+  a.ntiles = (int)ntiles;
+  a.nchunk = (int)nchunk;
+  a.ncb = (int)ncb;
+  hipLaunchKernelGGL((x3::conv3x3_igemm_kernel<G, EPI>), dim3((unsigned)grid),
+                     dim3(G::NTHR), 0, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(X3_EHIP, "conv kernel launch failed: %s", hipGetErrorString(e));
+  return X3_OK;
+}
+
+// Kernel configurations.  All use 8 wavefronts (512 threads, one workgroup
+// per CU because of the ~120-140 KB double-buffered LDS stage), CC = 8 input
+// channels per K chunk, and wave tiles of 128 accumulators (MT x NW = 8
+// MFMA blocks).  The tile width follows the output width.
+
+// 64-channel blocks: 2 channel blocks x 4 N-tiles per wave, TH*NCT = 32.
+template <int EPI, bool X4>
+x3_status dispatch_mt2(const x3::ConvArgs& a, hipStream_t st) {
+  if (a.Wo > 128) return run_conv<x3::Geo<2, 8, 4, 8, 8, X4>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8, X4>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8, X4>, EPI>(a, st);
+  return run_conv<x3::Geo<2, 8, 32, 1, 8, X4>, EPI>(a, st);
+}
+
+// 128-channel blocks: 4 channel blocks x 2 N-tiles per wave, TH*NCT = 16.
+template <int EPI, bool X4>
+x3_status dispatch_mt4(const x3::ConvArgs& a, hipStream_t st) {
+  if (a.Wo > 128) return run_conv<x3::Geo<4, 8, 2, 8, 8, X4>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<4, 8, 4, 4, 8, X4>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<4, 8, 8, 2, 8, X4>, EPI>(a, st);
+  return run_conv<x3::Geo<4, 8, 16, 1, 8, X4>, EPI>(a, st);
+}
+
+template <int EPI>
+x3_status dispatch(const x3::ConvArgs& a, hipStream_t st) {
+  const bool x4 = rows_aligned16(a);
+  if (channel_block_mt(a.Cout) == 4)
+    return x4 ? dispatch_mt4<EPI, true>(a, st) : dispatch_mt4<EPI, false>(a, st);
+  return x4 ? dispatch_mt2<EPI, true>(a, st) : dispatch_mt2<EPI, false>(a, st);
+}
+
+// Per-epilogue launchers, one translation unit each.
+x3_status launch_min_tanh2(const x3::ConvArgs& a, hipStream_t st);
+x3_status launch_mul_lrelu_gelu(const x3::ConvArgs& a, hipStream_t st);
+x3_status launch_scale_min(const x3::ConvArgs& a, hipStream_t st);
+// GroupNorm path: the conv pass (partials + pooled extrema), then the
+// finalize pass over B*groups workgroups.
+x3_status launch_gn_pool(const x3::ConvArgs& a, hipStream_t st);
+x3_status launch_gn_finalize(const x3::GnFinArgs& f, int nblocks,
+                             hipStream_t st);
+// GroupNorm partial slots per (sample, group) for this shape: one per
+// wavefront tile of the configuration launch_gn_pool picks.
+int gn_pps(int Ho, int Wo, int Cin, int Cout);
+
+}  // namespace x3i
