@@ -111,8 +111,8 @@ size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W, int Cout,
  * overwritten, and two calls sharing one workspace must be ordered on one
  * stream.  Two kernels are enqueued on `stream` (statistics + window
  * extrema, then finalize); `out` holds intermediate values between them.
- * Supported: Cout / groups == 4 (any Cout up to 1024 that is a multiple of
- * 4), pool_k == 4 (else X3_EUNSUPPORTED);
+ * Supported: any groups dividing Cout (Cout <= 1024), pool_k == 4 (else
+ * X3_EUNSUPPORTED);
  * eps > 0 and finite lo <= hi (else X3_EINVAL); Ho, Wo >= pool_k (else
  * X3_ESHAPE). */
 x3_status x3_conv3x3_gn_scale_pool_clamp_f32(

@@ -121,7 +121,10 @@ def test_gn_workspace_bytes(lib):
     assert f(2, 16, 128, 128, 64, 16, 4) == 2 * 16 * 128 * 16
     assert f(0, 8, 128, 128, 64, 16, 4) == 0
     assert f(2, 8, 128, 128, 64, 15, 4) == 0   # 64 % 15
-    assert f(2, 8, 128, 128, 64, 8, 4) == 0    # 8 channels per group: not compiled
+    # 8 channels per group: per-channel partials, 8 per group and slot
+    assert f(2, 8, 128, 128, 64, 8, 4) == 2 * 8 * 8 * 128 * 16
+    # one group of all 64 channels
+    assert f(2, 8, 128, 128, 64, 1, 4) == 2 * 1 * 64 * 128 * 16
     assert f(2, 8, 128, 128, 64, 16, 3) == 0   # pool 3: not compiled
     assert f(2, 8, 5, 5, 64, 16, 4) == 0       # 3x3 conv output < pool window
     assert f(2, 8, 128, 128, 1028, 257, 4) == 0  # Cout above 1024
@@ -147,7 +150,7 @@ def test_gn_validation(lib):
     assert call(k=0) == EINVAL
     assert call(groups=5) == ESHAPE
     assert call(H=5) == ESHAPE
-    assert call(groups=8) == EUNSUP
+    assert call(groups=8) == EWS  # supported; needs per-channel partials
     assert call(k=2) == EUNSUP
     assert call(Cout=1028, groups=257) == EUNSUP
     # Cout 128 is supported, but needs a workspace for 32 groups

@@ -443,3 +443,37 @@ def test_misaligned_buffers_take_the_scalar_paths():
     out = x3.conv3x3_scale_min(xb2[1:].view_as(g2["x"]), g2["weight"], g2["bias"], 2.0)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), run_oracle("scale_min", d2), what="x misaligned")
+
+
+# GroupNorm with other group sizes (per-channel partials merged by the
+# finalize): one group of all channels, 8, 2 and 1 channels per group at
+# Cout 64; 16 groups of 8 at Cout 128; odd sizes 6, 16, 25 and 3.
+GN_GROUPINGS = [  # (Cout, groups)
+    (64, 1), (64, 8), (64, 32), (64, 64), (128, 16), (96, 16), (48, 3), (200, 8), (12, 4),
+]
+
+
+@pytest.mark.parametrize("cg", GN_GROUPINGS)
+@pytest.mark.parametrize("shape", [(2, 8, 34, 34), (1, 12, 22, 131)])
+def test_gn_pool_any_group_size(cg, shape):
+    Cout, groups = cg
+    B, Cin, H, W = shape
+    say(f"gn_pool {shape} Cout={Cout} groups={groups}")
+    d = random_case("gn_scale_pool_clamp", B, Cin, H, W, Cout, seed=1300 + Cout + groups)
+    d["scale"][1::5] *= -1.0
+    kw = dict(groups=groups, lo=-50.0, hi=50.0)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw),
+                 run_oracle("gn_scale_pool_clamp", d, **kw), what=f"Cout={Cout} groups={groups}")
+
+
+def test_gn_pool_any_group_size_constant_channels():
+    """x == 1, w == 1 with 8 channels per group: every channel is constant,
+    so each per-channel partial has zero spread about its shift."""
+    d = random_case("gn_scale_pool_clamp", 1, 8, 20, 20, 64, seed=1400)
+    d["x"] = torch.ones_like(d["x"])
+    d["weight"] = torch.ones_like(d["weight"])
+    g = torch.Generator().manual_seed(1401)
+    d["bias"] = torch.randint(-16, 17, (64,), generator=g).float() / 64.0
+    kw = dict(groups=8, lo=-100.0, hi=100.0)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw),
+                 run_oracle("gn_scale_pool_clamp", d, **kw), what="all ones, 8 per group")

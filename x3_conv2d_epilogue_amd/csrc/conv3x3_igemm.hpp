@@ -52,6 +52,9 @@
 namespace x3 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define X3_LDS __attribute__((address_space(3)))
 // Every helper lambda of the kernel must inline: they capture the
@@ -63,7 +66,10 @@ enum Epilogue : int {
   EPI_MIN_TANH2 = 0,       // tanh(tanh(min_co y))
   EPI_MUL_LRELU_GELU = 1,  // gelu_erf(lrelu(y * mult[co]))
   EPI_SCALE_MIN = 2,       // min_co(scale * y)
-  EPI_GN_POOL = 3          // GroupNorm partials + pooling-window extrema
+  EPI_GN_POOL = 3,         // GroupNorm partials per group of 4 channels
+                           // + pooling-window extrema
+  EPI_GN_POOL_CH = 4       // GroupNorm partials per channel (any group
+                           // size) + pooling-window extrema
 };
 
 // Kernel arguments (plain values, passed by value).
@@ -72,19 +78,19 @@ struct ConvArgs {
   const float* w;
   const float* b;
   float* out;
-  const float* v0;  // mult (EPI_MUL_LRELU_GELU) | gamma (EPI_GN_POOL)
-  const float* v1;  // beta  (EPI_GN_POOL)
-  const float* v2;  // scale (EPI_GN_POOL)
+  const float* v0;  // mult (EPI_MUL_LRELU_GELU) | gamma (EPI_GN_POOL*)
+  const float* v1;  // beta  (EPI_GN_POOL*)
+  const float* v2;  // scale (EPI_GN_POOL*)
   float s0;         // neg_slope (EPI_MUL_LRELU_GELU) | scale (EPI_SCALE_MIN)
-  float4* part;     // GroupNorm partials (EPI_GN_POOL)
+  float4* part;     // GroupNorm partials (EPI_GN_POOL*)
   int B, Cin, H, W, Cout;
   int Ho, Wo;
   int n_rt, n_ct;   // row tiles, column tiles per sample
   int ntiles;       // B * n_rt * n_ct
   int nchunk;       // ceil(Cin / CC)
   int ncb;          // channel-block passes per tile: ceil(Cout / COUT)
-  int Ph, Pw;       // pooled output size (EPI_GN_POOL)
-  int groups;       // GroupNorm groups (EPI_GN_POOL)
+  int Ph, Pw;       // pooled output size (EPI_GN_POOL*)
+  int groups;       // GroupNorm groups (EPI_GN_POOL*)
 };
 
 // Largest Cout: per-channel constants of all channel blocks live in LDS.
@@ -196,6 +202,8 @@ __device__ __forceinline__ float erf_as(float x) {
 enum : int {
   DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
   DPP_QUAD_XOR2 = 0x4E,  // quad_perm [2,3,0,1]
+  DPP_ROW_MIRROR = 0x140,       // lane i of a row of 16 <- lane 15 - i
+  DPP_ROW_HALF_MIRROR = 0x141,  // lane i of a half-row of 8 <- lane 7 - i
   DPP_ROW_ROR4 = 0x124,  // rotate a row of 16 by 4
   DPP_ROW_ROR8 = 0x128   // rotate a row of 16 by 8
 };
@@ -418,7 +426,7 @@ __global__ void __launch_bounds__(G::NTHR)
     if (real) {
       bv = a.b[co];
       if constexpr (EPI == EPI_MUL_LRELU_GELU) pv = a.v0[co];
-      if constexpr (EPI == EPI_GN_POOL)
+      if constexpr (EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH)
         pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : 0.0f;
     }
     s_bias[co] = bv;
@@ -524,8 +532,8 @@ __global__ void __launch_bounds__(G::NTHR)
                 __builtin_bit_cast(uint32_t, y), o_rsrc, off, 0, 0);
           }
         }
-    } else {  // EPI_GN_POOL: requires NW == 4, Cout/groups == 4, pool 4
-      static_assert(EPI != EPI_GN_POOL || G::NW == 4, "pool needs 4 rows");
+    } else {  // EPI_GN_POOL(_CH): requires NW == 4 and pool 4
+      static_assert(G::NW == 4, "pool needs 4 rows");
       // Stores go through raw buffer resources over this sample's slice of
       // `part` and `out`; a store that must not happen gets bit 31 set in
       // its offset (past num_records, dropped by the hardware), so the
@@ -535,9 +543,6 @@ __global__ void __launch_bounds__(G::NTHR)
       // (padded channels and groups land past the ends and are dropped)
       const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
           a.out + (size_t)n * a.Cout * PP, (uint32_t)(a.Cout * PP * 4));
-      const __amdgpu_buffer_rsrc_t p_rsrc =
-          make_rsrc(a.part + (size_t)n * a.groups * pps,
-                    (uint32_t)(a.groups * pps * 16));
       // (1) GroupNorm partials of this wave: per group, the count, the sum
       // and the sum of squared deviations from the wave's own group mean,
       // over the wave's valid pixels.  A group is 4 consecutive channels,
@@ -549,6 +554,11 @@ __global__ void __launch_bounds__(G::NTHR)
       nrow_ok = nrow_ok < 0 ? 0 : (nrow_ok > G::NW ? G::NW : nrow_ok);
       int ncol_ok = a.Wo - (ct * G::TWC + wm.strip * 32);
       ncol_ok = ncol_ok < 0 ? 0 : (ncol_ok > 32 ? 32 : ncol_ok);
+      const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
+      if constexpr (EPI == EPI_GN_POOL) {
+      const __amdgpu_buffer_rsrc_t p_rsrc =
+          make_rsrc(a.part + (size_t)n * a.groups * pps,
+                    (uint32_t)(a.groups * pps * 16));
       const float cnt = (float)(4 * nrow_ok * ncol_ok);
       const float inv_cnt = cnt > 0.0f ? 1.0f / cnt : 0.0f;
       float my_sum = 0.0f, my_m2 = 0.0f;  // lane l32 = mt*4+q keeps (mt, q)
@@ -577,12 +587,91 @@ __global__ void __launch_bounds__(G::NTHR)
       {
         // lane (h, l32 = mt*4+q) writes group g = co0/4 + mt*8 + 2q + h
         const int g = (co0 >> 2) + (l32 >> 2) * 8 + 2 * (l32 & 3) + h;
-        const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
         const uint32_t off = ((uint32_t)(g * pps + slot) << 4) |
                              ((uint32_t)(l32 >= G::MT * 4) << 31);
         const float4 v = make_float4(my_sum, my_m2, cnt, 0.0f);
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(u32x4, v), p_rsrc, off, 0, 0);
+      }
+      } else {
+      // (1') Per-channel partials (any group size; the finalize merges the
+      // group's channels): count, sum and M2 of each channel over the
+      // wave's valid pixels, again about a shift K, the channel's value at
+      // the wave's first pixel.  In-lane over the rows, then across the 32
+      // columns of a lane half, 8 accumulator elements at a time, by a
+      // halving exchange: in each of 3 steps a lane keeps half of its
+      // channel sums, adds the partner's matching half and hands over the
+      // other half.  The partners are l^16, l^15, l^7 (swizzle, row mirror,
+      // half-row mirror) and the keep decision is lane bit 4, 3, 2; two
+      // quad steps (l^1, l^2) complete the sums.  Each quad ends with
+      // element (l32 >> 2) & 7 of the 8, and its first lane stores it.
+      const __amdgpu_buffer_rsrc_t p_rsrc =
+          make_rsrc(a.part + (size_t)n * a.Cout * pps,
+                    (uint32_t)(a.Cout * pps * 16));
+      const float cnt = (float)(nrow_ok * ncol_ok);
+      const float inv_cnt = cnt > 0.0f ? 1.0f / cnt : 0.0f;
+      const bool b4 = (l32 >> 4) & 1, b3 = (l32 >> 3) & 1, b2 = (l32 >> 2) & 1;
+      const int e8 = (l32 >> 2) & 7;
+      const uint32_t not_lead = (uint32_t)((l32 & 3) != 0) << 31;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          // (vector values, not arrays: selects between array elements
+          // would be turned into loads from selected addresses, which
+          // keeps the arrays in scratch memory)
+          f32x8 s1, s2, kv;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int i = 8 * hs + k;
+            const float K = half_lane0(acc[mt][0][i], h);
+            kv[k] = K;
+            float u1 = 0.0f, u2 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < G::NW; ++j) {
+              const float d = (col_ok && j < nrow_ok) ? acc[mt][j][i] - K : 0.0f;
+              u1 += d;
+              u2 = fmaf(d, d, u2);
+            }
+            s1[k] = u1;
+            s2[k] = u2;
+          }
+          // partner l^16, keep by bit 4
+          f32x4 t1 = b4 ? s1.hi : s1.lo, t2 = b4 ? s2.hi : s2.lo;
+          const f32x4 g1 = b4 ? s1.lo : s1.hi, g2 = b4 ? s2.lo : s2.hi;
+          const f32x4 kv4 = b4 ? kv.hi : kv.lo;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            t1[k] += swz_xor16(g1[k]);
+            t2[k] += swz_xor16(g2[k]);
+          }
+          // partner l^15, keep by bit 3
+          f32x2 r1 = b3 ? t1.hi : t1.lo, r2 = b3 ? t2.hi : t2.lo;
+          const f32x2 h1 = b3 ? t1.lo : t1.hi, h2 = b3 ? t2.lo : t2.hi;
+          const f32x2 kv2 = b3 ? kv4.hi : kv4.lo;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            r1[k] += dpp<DPP_ROW_MIRROR>(h1[k]);
+            r2[k] += dpp<DPP_ROW_MIRROR>(h2[k]);
+          }
+          // partner l^7, keep by bit 2; then the quad
+          float S1 = (b2 ? r1.y : r1.x) + dpp<DPP_ROW_HALF_MIRROR>(b2 ? r1.x : r1.y);
+          float S2 = (b2 ? r2.y : r2.x) + dpp<DPP_ROW_HALF_MIRROR>(b2 ? r2.x : r2.y);
+          S1 += dpp<DPP_QUAD_XOR1>(S1);
+          S2 += dpp<DPP_QUAD_XOR1>(S2);
+          S1 += dpp<DPP_QUAD_XOR2>(S1);
+          S2 += dpp<DPP_QUAD_XOR2>(S2);
+          const float K = b2 ? kv2.y : kv2.x;
+          // element i = 8*hs + e8 is channel 8*(i>>2) + 4h + (i&3) of block mt
+          const int co =
+              co0 + mt * 32 + 8 * (2 * hs + (e8 >> 2)) + 4 * h + (e8 & 3);
+          const float4 v = make_float4(fmaf(K, cnt, S1),
+                                       fmaxf(S2 - S1 * S1 * inv_cnt, 0.0f), cnt,
+                                       0.0f);
+          const uint32_t off = ((uint32_t)(co * pps + slot) << 4) | not_lead;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4, v), p_rsrc, off, 0, 0);
+        }
       }
       // (2) 4x4 window extrema.  The wave's 4 N-tiles are 4 consecutive
       // rows starting at a multiple of 4, and 4 consecutive lanes are 4
@@ -747,10 +836,12 @@ __global__ void __launch_bounds__(G::NTHR)
 }
 
 // ---------------------------------------------------------------------------
-// GroupNorm finalize: merge the per-wave partials of one (sample, group)
-// in double, then normalize, apply the affine and the per-channel scale,
-// and clamp, in place on the pooled extrema written by
-// conv3x3_igemm_kernel<..., EPI_GN_POOL>.
+// GroupNorm finalize: merge the partials of one (sample, group) in double,
+// then normalize, apply the affine and the per-channel scale, and clamp, in
+// place on the pooled extrema written by conv3x3_igemm_kernel<...,
+// EPI_GN_POOL or EPI_GN_POOL_CH>.  The group's partials are `pps`
+// consecutive float4 (per-wave partials of the group, or of each of its
+// channels in turn).
 struct GnFinArgs {
   const float4* part;
   const float* gamma;
@@ -758,7 +849,7 @@ struct GnFinArgs {
   const float* scale;
   float* out;
   int groups, cpg;   // groups, channels per group
-  int pps;           // partial slots per (sample, group)
+  int pps;           // partials per (sample, group)
   int plane;         // Ph * Pw
   float eps, lo, hi;
   double count;      // elements per group: cpg * Ho * Wo
@@ -778,9 +869,10 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
   return t;
 }
 
-// One workgroup of NT threads per (sample, group).  The group's 4 pooled
-// channel planes are one contiguous block of 4*plane floats in `out`; with
-// VEC (block 16-byte aligned) it is moved as float4.
+// One workgroup of NT threads per (sample, group).  The group's cpg pooled
+// channel planes are one contiguous block of cpg*plane floats in `out`;
+// with up to 4 channels and VEC (block 16-byte aligned) it is moved as
+// float4, larger groups go channel by channel.
 //
 // Merge: every partial k holds (sum_k, M2_k, n_k) over its pixels, with
 // M2_k taken about its own mean.  With N = sum n_k (known: channels x Ho x
@@ -831,9 +923,22 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
   // z = ((v - mu) * rstd * gamma + beta) * scale = (v - mu) * A + Bc, with
   // A = rstd*gamma*scale and Bc = beta*scale per channel; monotone in v
   // with the sign of gamma*scale, as the pooling pass assumed.
-  // Per-channel constants as plain scalars, selected per element (an
-  // indexed array or struct here ends up in LDS or scratch memory).
   const int c0 = g * a.cpg;
+  const float lo = a.lo, hi = a.hi;
+  if (a.cpg > 4) {
+    // any group size: channel by channel
+    for (int c = 0; c < a.cpg; ++c) {
+      const float A = rstd * a.gamma[c0 + c] * a.scale[c0 + c];
+      const float Bc = a.beta[c0 + c] * a.scale[c0 + c];
+      float* oc = o + (size_t)c * a.plane;
+      for (int k = tid; k < a.plane; k += NT)
+        oc[k] = fminf(fmaxf(fmaf(oc[k] - mu, A, Bc), lo), hi);
+    }
+    return;
+  }
+  // Up to 4 channels: per-channel constants as plain scalars, selected per
+  // element (an indexed array or struct here ends up in LDS or scratch
+  // memory).
   const int c1 = c0 + (a.cpg > 1), c2 = c0 + 2 * (a.cpg > 2),
             c3 = c0 + 3 * (a.cpg > 3);
   const float A0 = rstd * a.gamma[c0] * a.scale[c0];
@@ -845,7 +950,6 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
   const float B2 = a.beta[c2] * a.scale[c2];
   const float B3 = a.beta[c3] * a.scale[c3];
   const int p1 = a.plane, p2 = 2 * a.plane, p3 = 3 * a.plane;
-  const float lo = a.lo, hi = a.hi;
 #define X3_GN_OUT(v, e)                                                     \
   fminf(fmaxf(fmaf((v) - mu,                                                \
                    (e) < p1 ? A0 : ((e) < p2 ? A1 : ((e) < p3 ? A2 : A3)), \

@@ -110,8 +110,18 @@ x3_status launch_scale_min(const x3::ConvArgs& a, hipStream_t st);
 x3_status launch_gn_pool(const x3::ConvArgs& a, hipStream_t st);
 x3_status launch_gn_finalize(const x3::GnFinArgs& f, int nblocks,
                              hipStream_t st);
-// GroupNorm partial slots per (sample, group) for this shape: one per
-// wavefront tile of the configuration launch_gn_pool picks.
+// GroupNorm partial slots per (sample, group or channel) for this shape: one
+// per wavefront tile of the configuration launch_gn_pool picks.
 int gn_pps(int Ho, int Wo, int Cin, int Cout);
+// Groups of 4 channels take per-group partials (one lane holds a whole
+// group); any other group size takes per-channel partials.
+inline bool gn_partials_per_channel(int Cout, int groups) {
+  return Cout / groups != 4;
+}
+// float4 partials per (sample, group) that the finalize merges.
+inline int gn_parts_per_group(int Ho, int Wo, int Cin, int Cout, int groups) {
+  const int slots = gn_pps(Ho, Wo, Cin, Cout);
+  return gn_partials_per_channel(Cout, groups) ? slots * (Cout / groups) : slots;
+}
 
 }  // namespace x3i

@@ -25,16 +25,14 @@ GnGeo gn_geo(int Wo, int Cin, int Cout) {
   return {32, 32, 8};
 }
 
-template <bool X4>
+template <bool X4, int EPI>
 x3_status dispatch_gn(const x3::ConvArgs& a, hipStream_t st) {
   if (gn_resident(a.Cin, a.Cout)) {
-    if (a.Wo > 64)
-      return run_conv<x3::Geo<2, 8, 4, 4, 4, X4, true>, x3::EPI_GN_POOL>(a, st);
-    if (a.Wo > 32)
-      return run_conv<x3::Geo<2, 8, 8, 2, 4, X4, true>, x3::EPI_GN_POOL>(a, st);
-    return run_conv<x3::Geo<2, 8, 16, 1, 4, X4, true>, x3::EPI_GN_POOL>(a, st);
+    if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 4, 4, 4, X4, true>, EPI>(a, st);
+    if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 8, 2, 4, X4, true>, EPI>(a, st);
+    return run_conv<x3::Geo<2, 8, 16, 1, 4, X4, true>, EPI>(a, st);
   }
-  return dispatch_mt2<x3::EPI_GN_POOL, X4>(a, st);
+  return dispatch_mt2<EPI, X4>(a, st);
 }
 
 }  // namespace
@@ -45,14 +43,18 @@ int gn_pps(int Ho, int Wo, int Cin, int Cout) {
 }
 
 x3_status launch_gn_pool(const x3::ConvArgs& a, hipStream_t st) {
-  return rows_aligned16(a) ? dispatch_gn<true>(a, st) : dispatch_gn<false>(a, st);
+  const bool x4 = rows_aligned16(a);
+  if (gn_partials_per_channel(a.Cout, a.groups))
+    return x4 ? dispatch_gn<true, x3::EPI_GN_POOL_CH>(a, st)
+              : dispatch_gn<false, x3::EPI_GN_POOL_CH>(a, st);
+  return x4 ? dispatch_gn<true, x3::EPI_GN_POOL>(a, st)
+            : dispatch_gn<false, x3::EPI_GN_POOL>(a, st);
 }
 
 x3_status launch_gn_finalize(const x3::GnFinArgs& f, int nblocks,
                              hipStream_t st) {
-  // Each group's pooled block moves as float4 when it is 16-byte aligned
-  // (4 channels per group make every block a multiple of 4 floats; `out`
-  // itself must be aligned).
+  // A group of up to 4 channels moves its pooled block as float4 when the
+  // block is 16-byte aligned (`out` aligned, block a multiple of 4 floats).
   if (((uintptr_t)f.out & 15u) == 0 && (f.cpg * f.plane) % 4 == 0)
     hipLaunchKernelGGL((x3::gn_finalize_kernel<256, true>), dim3((unsigned)nblocks),
                        dim3(256), 0, st, f);

@@ -191,21 +191,20 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
                 H - 2, W - 2);
   if (Cout > x3::kMaxCout)
     return fail(X3_EUNSUPPORTED, "Cout=%d exceeds %d", Cout, x3::kMaxCout);
-  if (Cout / groups != 4)
-    return fail(X3_EUNSUPPORTED,
-                "GroupNorm path: %d channels per group not compiled in (4)",
-                Cout / groups);
   if (pool_k != 4)
     return fail(X3_EUNSUPPORTED, "pool_k=%d not compiled in (4)", pool_k);
   if ((uint64_t)Cin * H * W * 4 >= (1ull << 31))
     return fail(X3_EUNSUPPORTED, "one sample of x must be smaller than 2 GiB");
   // (the kernel works in 64-channel blocks: padded channels and groups
-  // must stay addressable too)
+  // must stay addressable too; partials are per group of 4 channels or per
+  // channel)
   const uint64_t P = (uint64_t)((H - 2 - pool_k) / pool_k + 1) *
                      ((W - 2 - pool_k) / pool_k + 1);
   const uint64_t cpad = (uint64_t)(Cout + 63) / 64 * 64;
+  const uint64_t prows =
+      x3i::gn_partials_per_channel(Cout, groups) ? cpad : cpad / 4;
   if (cpad * P * 4 >= (1ull << 31) ||
-      cpad / 4 * x3i::gn_pps(H - 2, W - 2, Cin, Cout) * 16 >= (1ull << 31))
+      prows * x3i::gn_pps(H - 2, W - 2, Cin, Cout) * 16 >= (1ull << 31))
     return fail(X3_EUNSUPPORTED,
                 "one sample of out or of the workspace must be < 2 GiB");
   s = Shape{B, Cin, H, W, Cout, H - 2, W - 2};
@@ -221,7 +220,8 @@ X3_API size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W,
   const x3_status rc = check_gn(B, Cin, H, W, Cout, groups, pool_k, s);
   __builtin_memcpy(g_err, saved, sizeof(g_err));
   if (rc != X3_OK) return 0;
-  return (size_t)B * groups * x3i::gn_pps(s.Ho, s.Wo, s.Cin, s.Cout) *
+  return (size_t)B * groups *
+         x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups) *
          sizeof(float4);
 }
 
@@ -243,7 +243,8 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
     return fail(X3_EINVAL, "clamp bounds must be finite with lo <= hi");
   if (B == 0) return X3_OK;
   const size_t need =
-      (size_t)B * groups * x3i::gn_pps(s.Ho, s.Wo, s.Cin, s.Cout) * sizeof(float4);
+      (size_t)B * groups *
+      x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups) * sizeof(float4);
   if (!workspace || workspace_bytes < need)
     return fail(X3_EWORKSPACE, "workspace of %zu bytes needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -280,7 +281,7 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   f.out = out;
   f.groups = groups;
   f.cpg = Cout / groups;
-  f.pps = x3i::gn_pps(s.Ho, s.Wo, s.Cin, s.Cout);
+  f.pps = x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups);
   f.plane = Ph * Pw;
   f.eps = eps;
   f.lo = lo;
