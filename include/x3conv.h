@@ -83,6 +83,24 @@ x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
                                         int Cin, int H, int W, int Cout,
                                         void* stream);
 
+/* Epilogue (b) with the tanh approximation of GELU that [P54] drafts before
+ * settling on the erf form: out = 0.5 * v * (1 + tanh(sqrt(2/pi) *
+ * (v + 0.044715 * v^3))), v as above.  Same arguments, layouts and errors
+ * as x3_conv3x3_mul_lrelu_gelu_f32. */
+x3_status x3_conv3x3_mul_lrelu_gelu_tanh_f32(const float* x, const float* w,
+                                             const float* b, const float* mult,
+                                             float neg_slope, float* out,
+                                             int B, int Cin, int H, int W,
+                                             int Cout, void* stream);
+
+/* The convolution alone (the first step of every epilogue above, [P32]
+ * opening analysis): y = conv3x3(x, w) + b, y: [B][Cout][Ho][Wo].  The
+ * starting point of the split path (the standalone epilogues below).  Same
+ * limits as x3_conv3x3_mul_lrelu_gelu_f32. */
+x3_status x3_conv3x3_bias_f32(const float* x, const float* w, const float* b,
+                              float* y, int B, int Cin, int H, int W, int Cout,
+                              void* stream);
+
 /* Epilogue (c), [P32]: out[n,0,h,w] = min_co (scale * y[n,co,h,w]).
  * The page uses scale = 2.0; any finite scale is accepted (for scale < 0 the
  * minimum of the scaled values is scale times the channel maximum).
@@ -107,12 +125,15 @@ size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W, int Cout,
  * gamma, beta, scale: [Cout].  out: [B][Cout][Ph][Pw] with
  * Ph = (Ho - pool_k) / pool_k + 1, Pw = (Wo - pool_k) / pool_k + 1.
  * workspace: device memory of at least x3_conv3x3_gn_workspace_bytes(...)
- * bytes, owned by the caller, contents need not be initialized; it is
- * overwritten, and two calls sharing one workspace must be ordered on one
- * stream.  Two kernels are enqueued on `stream` (statistics + window
- * extrema, then finalize); `out` holds intermediate values between them.
- * Supported: any groups dividing Cout (Cout <= 1024), pool_k == 4 (else
- * X3_EUNSUPPORTED);
+ * bytes, 16-byte aligned, owned by the caller, contents need not be
+ * initialized; it is overwritten, and two calls sharing one workspace must
+ * be ordered on one stream.  Two kernels are enqueued on `stream`.  With
+ * pool_k == 4 the conv kernel writes statistics partials (workspace) and
+ * the window extrema (out), then a finalize normalizes out in place.  Any
+ * other pool_k takes the split path: the conv output goes to the workspace
+ * (B*Cout*Ho*Wo floats), then x3_epi_gn_scale_pool_clamp_f32's kernel runs
+ * on it.
+ * Supported: any groups dividing Cout (Cout <= 1024), any pool_k >= 1;
  * eps > 0 and finite lo <= hi (else X3_EINVAL); Ho, Wo >= pool_k (else
  * X3_ESHAPE). */
 x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
@@ -120,6 +141,49 @@ x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
     const float* beta, const float* scale, int groups, float eps, int pool_k,
     float lo, float hi, float* out, void* workspace, size_t workspace_bytes,
     int B, int Cin, int H, int W, int Cout, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Standalone epilogues over a stored conv output y [B][C][H][W] (NCHW,
+ * fp32, device memory owned by the caller).  Each is one HBM-bound kernel;
+ * together with x3_conv3x3_bias_f32 they are the unfused form of the fused
+ * entry points above (the split strategy that all four pages adopt), and
+ * they apply to a convolution computed elsewhere.  Sizes: B >= 0, C, H, W
+ * >= 1 (else X3_EINVAL); B == 0 enqueues nothing.  out must not overlap an
+ * input (the GELU forms allow out == y exactly).
+ * ------------------------------------------------------------------------ */
+
+/* [P25]: out[n,0,h,w] = tanh(tanh(min_c y[n,c,h,w])); out [B][1][H][W]. */
+x3_status x3_epi_min_tanh2_f32(const float* y, float* out, int B, int C, int H,
+                               int W, void* stream);
+
+/* [P32]: out[n,0,h,w] = min_c (scale * y[n,c,h,w]); out [B][1][H][W]; scale
+ * finite (else X3_EINVAL). */
+x3_status x3_epi_scale_min_f32(const float* y, float scale, float* out, int B,
+                               int C, int H, int W, void* stream);
+
+/* [P54]: out = gelu_erf(lrelu(y * mult[c], neg_slope)), elementwise;
+ * mult [C]; out [B][C][H][W], may be y. */
+x3_status x3_epi_mul_lrelu_gelu_f32(const float* y, const float* mult,
+                                    float neg_slope, float* out, int B, int C,
+                                    int H, int W, void* stream);
+
+/* As above with the tanh approximation of GELU. */
+x3_status x3_epi_mul_lrelu_gelu_tanh_f32(const float* y, const float* mult,
+                                         float neg_slope, float* out, int B,
+                                         int C, int H, int W, void* stream);
+
+/* [P85]: GroupNorm(groups, eps, gamma, beta) -> * scale[c] ->
+ * MaxPool2d(pool_k, stride pool_k, floor) -> clamp[lo, hi], as
+ * x3_conv3x3_gn_scale_pool_clamp_f32 defines it, on y.  out [B][C][Ph][Pw],
+ * Ph = (H - pool_k) / pool_k + 1, Pw likewise.  groups must divide C and
+ * H, W >= pool_k (else X3_ESHAPE); eps > 0, finite lo <= hi (else
+ * X3_EINVAL).  No workspace: one workgroup per (sample, group) computes the
+ * statistics and then the group's pooled outputs. */
+x3_status x3_epi_gn_scale_pool_clamp_f32(const float* y, const float* gamma,
+                                         const float* beta, const float* scale,
+                                         int groups, float eps, int pool_k,
+                                         float lo, float hi, float* out, int B,
+                                         int C, int H, int W, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* x3_status_str(x3_status s);

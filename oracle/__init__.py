@@ -41,6 +41,8 @@ def _load():
         "x3o_min_tanh2": [_f32p, _f32p, _f32p, _f64p, _int, _int, _int, _int, _int],
         "x3o_min_tanh2_at": [_f32p, _f32p, _f32p, _int, _int, _int, _int, _i64p, _i64, _f64p],
         "x3o_mul_lrelu_gelu": [_f32p, _f32p, _f32p, _f32p, _dbl, _f64p, _int, _int, _int, _int, _int],
+        "x3o_mul_lrelu_gelu_tanh": [_f32p, _f32p, _f32p, _f32p, _dbl, _f64p, _int, _int, _int,
+                                    _int, _int],
         "x3o_mul_lrelu_gelu_at": [_f32p, _f32p, _f32p, _f32p, _dbl, _int, _int, _int, _i64p, _i64, _f64p],
         "x3o_scale_min": [_f32p, _f32p, _f32p, _dbl, _f64p, _int, _int, _int, _int, _int],
         "x3o_scale_min_at": [_f32p, _f32p, _f32p, _dbl, _int, _int, _int, _int, _i64p, _i64, _f64p],
@@ -114,6 +116,17 @@ def mul_lrelu_gelu(x, w, b, mult, slope=0.01) -> np.ndarray:
     out = np.empty((B, Cout, H - 2, W - 2), dtype=np.float64)
     lib.x3o_mul_lrelu_gelu(xp, wp, bp, mp, float(slope), out.ctypes.data_as(_f64p),
                            B, Cin, H, W, Cout)
+    return out
+
+
+def mul_lrelu_gelu_tanh(x, w, b, mult, slope=0.01) -> np.ndarray:
+    """gelu_tanh(leaky_relu(conv * mult[c], slope)), [B, Cout, H-2, W-2]."""
+    lib = _load()
+    x, xp = _f32(x); w, wp = _f32(w); b, bp = _f32(b); m, mp = _f32(mult)
+    B, Cin, H, W, Cout = _shape(x, w)
+    out = np.empty((B, Cout, H - 2, W - 2), dtype=np.float64)
+    lib.x3o_mul_lrelu_gelu_tanh(xp, wp, bp, mp, float(slope), out.ctypes.data_as(_f64p),
+                                B, Cin, H, W, Cout)
     return out
 
 

@@ -143,6 +143,33 @@ X3O_EXPORT void x3o_mul_lrelu_gelu(const float* x, const float* wt,
               slope);
 }
 
+/* Epilogue (b) with the tanh approximation of GELU, which [P54] drafts
+ * first (before switching to the erf form):
+ *   0.5 * v * (1 + tanh(sqrt(2/pi) * (v + 0.044715 * v^3))),
+ * v = LeakyReLU(y * m[co]) as above.  out [B][Cout][Ho][Wo]. */
+static double mul_lrelu_gelu_tanh_of(double y, double m, double slope) {
+  double v = y * m;
+  v = (v >= 0.0) ? v : slope * v;
+  const double pi = 3.14159265358979323846;
+  return 0.5 * v * (1.0 + tanh(sqrt(2.0 / pi) * (v + 0.044715 * v * v * v)));
+}
+
+X3O_EXPORT void x3o_mul_lrelu_gelu_tanh(const float* x, const float* wt,
+                                        const float* bias, const float* mult,
+                                        double slope, double* out, int B,
+                                        int Cin, int H, int W, int Cout) {
+  const int Ho = H - 2, Wo = W - 2;
+  if (B <= 0 || Ho <= 0 || Wo <= 0) return;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t n = 0; n < B; ++n)
+    for (int co = 0; co < Cout; ++co)
+      for (int h = 0; h < Ho; ++h)
+        for (int w = 0; w < Wo; ++w)
+          out[idx4(n, co, h, w, Cout, Ho, Wo)] = mul_lrelu_gelu_tanh_of(
+              conv_at(x, wt, bias, Cin, H, W, n, co, h, w), (double)mult[co],
+              slope);
+}
+
 /* Sampled form: el holds `count` quadruples (n, co, h, w). */
 X3O_EXPORT void x3o_mul_lrelu_gelu_at(const float* x, const float* wt,
                                       const float* bias, const float* mult,

@@ -125,7 +125,10 @@ def test_gn_workspace_bytes(lib):
     assert f(2, 8, 128, 128, 64, 8, 4) == 2 * 8 * 8 * 128 * 16
     # one group of all 64 channels
     assert f(2, 8, 128, 128, 64, 1, 4) == 2 * 1 * 64 * 128 * 16
-    assert f(2, 8, 128, 128, 64, 16, 3) == 0   # pool 3: not compiled
+    # other pool windows take the split path: the workspace holds the conv
+    # output, [2, 64, 126, 126] floats
+    assert f(2, 8, 128, 128, 64, 16, 3) == 2 * 64 * 126 * 126 * 4
+    assert f(2, 8, 128, 128, 64, 16, 0) == 0   # pool 0: invalid
     assert f(2, 8, 5, 5, 64, 16, 4) == 0       # 3x3 conv output < pool window
     assert f(2, 8, 128, 128, 1028, 257, 4) == 0  # Cout above 1024
 
@@ -151,7 +154,7 @@ def test_gn_validation(lib):
     assert call(groups=5) == ESHAPE
     assert call(H=5) == ESHAPE
     assert call(groups=8) == EWS  # supported; needs per-channel partials
-    assert call(k=2) == EUNSUP
+    assert call(k=2) == EWS   # split path: the workspace must hold the conv output
     assert call(Cout=1028, groups=257) == EUNSUP
     # Cout 128 is supported, but needs a workspace for 32 groups
     assert call(Cout=128, groups=32) == EWS
@@ -178,3 +181,54 @@ def test_python_binding_rejects_cpu_tensors():
         x3.conv3x3_min_tanh2(x, w, b)
     with pytest.raises(TypeError):
         x3.conv3x3_scale_min(x.double(), w, b)
+
+
+def test_conv_bias_and_tanh_gelu_validation(lib):
+    s = P(0)
+    f = lib.x3_conv3x3_bias_f32
+    assert f(X, W_, B_, O, -1, 16, 32, 32, 64, s) == EINVAL
+    assert f(X, W_, B_, O, 2, 16, 2, 32, 64, s) == ESHAPE
+    assert f(X, W_, B_, O, 2, 16, 32, 32, 1025, s) == EUNSUP
+    assert f(X, W_, B_, X, 2, 16, 32, 32, 64, s) == EINVAL   # y aliases x
+    assert f(None, W_, B_, None, 0, 16, 32, 32, 64, s) == OK
+    g = lib.x3_conv3x3_mul_lrelu_gelu_tanh_f32
+    assert g(X, W_, B_, None, 0.01, O, 2, 16, 32, 32, 64, s) == EINVAL
+    assert g(X, W_, B_, M, float("nan"), O, 2, 16, 32, 32, 64, s) == EINVAL
+    assert g(None, W_, B_, M, 0.01, None, 0, 16, 32, 32, 64, s) == OK
+
+
+def test_standalone_epilogue_validation(lib):
+    s = P(0)
+    Y = fake(0x10000000)
+    assert lib.x3_epi_min_tanh2_f32(Y, O, -1, 4, 8, 8, s) == EINVAL
+    assert lib.x3_epi_min_tanh2_f32(Y, O, 2, 0, 8, 8, s) == EINVAL
+    assert lib.x3_epi_min_tanh2_f32(None, O, 2, 4, 8, 8, s) == EINVAL
+    assert lib.x3_epi_min_tanh2_f32(Y, Y, 2, 4, 8, 8, s) == EINVAL   # out overlaps y
+    assert lib.x3_epi_min_tanh2_f32(None, None, 0, 4, 8, 8, s) == OK
+    assert lib.x3_epi_scale_min_f32(Y, float("inf"), O, 2, 4, 8, 8, s) == EINVAL
+    for name in ("x3_epi_mul_lrelu_gelu_f32", "x3_epi_mul_lrelu_gelu_tanh_f32"):
+        f = getattr(lib, name)
+        assert f(Y, None, 0.01, O, 2, 4, 8, 8, s) == EINVAL
+        assert f(Y, M, float("nan"), O, 2, 4, 8, 8, s) == EINVAL
+        # partial overlap of out and y is refused
+        assert f(Y, M, 0.01, fake(0x10000010), 2, 4, 8, 8, s) == EINVAL
+        assert f(None, M, 0.01, None, 0, 4, 8, 8, s) == OK
+    f = lib.x3_epi_gn_scale_pool_clamp_f32
+    G_, BE, SC = M, fake(0x51000000), fake(0x52000000)
+
+    def call(**kw):
+        a = dict(y=Y, g=G_, be=BE, sc=SC, groups=4, eps=1e-5, k=4, lo=0.0, hi=1.0, out=O,
+                 B=2, C=16, H=32, W=32)
+        a.update(kw)
+        return f(a["y"], a["g"], a["be"], a["sc"], a["groups"], a["eps"], a["k"], a["lo"],
+                 a["hi"], a["out"], a["B"], a["C"], a["H"], a["W"], s)
+
+    assert call(groups=0) == EINVAL
+    assert call(k=0) == EINVAL
+    assert call(groups=3) == ESHAPE
+    assert call(H=3) == ESHAPE          # smaller than the window
+    assert call(eps=0.0) == EINVAL
+    assert call(lo=2.0) == EINVAL
+    assert call(sc=None) == EINVAL
+    assert call(out=Y) == EINVAL
+    assert call(B=0, y=None, out=None) == OK

@@ -197,6 +197,33 @@ def test_mul_lrelu_gelu_textbook_constants():
     assert out[2] == 0.0
 
 
+@pytest.mark.parametrize("shape", SMALL_SHAPES)
+def test_mul_lrelu_gelu_tanh_matches_torch(shape):
+    """The tanh-approximation form against torch's own tanh GELU in float64."""
+    B, Cin, H, W, Cout = shape
+    d = _np(random_case("mul_lrelu_gelu", B, Cin, H, W, Cout, seed=32))
+    out = oracle.mul_lrelu_gelu_tanh(d["x"], d["weight"], d["bias"], d["multiplier"], 0.01)
+    y = _torch_conv64(d["x"], d["weight"], d["bias"])
+    m = torch.from_numpy(d["multiplier"]).double().view(1, -1, 1, 1)
+    ref = F.gelu(F.leaky_relu(y * m, negative_slope=0.01), approximate="tanh").numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_mul_lrelu_gelu_tanh_identities():
+    """g(v) - g(-v) = v for g = 0.5 v (1 + tanh(u(v))) with u odd; g(0) = 0;
+    and the approximation stays within 1e-3 of the exact GELU."""
+    v = np.linspace(-6.0, 6.0, 241).astype(np.float32)
+    x = np.zeros((1, 1, 3, 3), np.float32)
+    w = np.zeros((v.size, 1, 3, 3), np.float32)
+    m = np.ones(v.size, np.float32)
+    pos = oracle.mul_lrelu_gelu_tanh(x, w, v, m, 1.0)[0, :, 0, 0]      # slope 1: no LReLU
+    neg = oracle.mul_lrelu_gelu_tanh(x, w, -v, m, 1.0)[0, :, 0, 0]
+    np.testing.assert_allclose(pos - neg, v.astype(np.float64), rtol=0, atol=1e-12)
+    assert pos[v.size // 2] == 0.0
+    exact = oracle.mul_lrelu_gelu(x, w, v, m, 1.0)[0, :, 0, 0]
+    assert np.abs(pos - exact).max() < 1e-3
+
+
 def test_mul_lrelu_gelu_sampled_matches_full():
     d = _np(random_case("mul_lrelu_gelu", 2, 3, 9, 10, 6, seed=2))
     full = oracle.mul_lrelu_gelu(d["x"], d["weight"], d["bias"], d["multiplier"])

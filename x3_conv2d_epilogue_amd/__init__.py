@@ -15,9 +15,11 @@ import os
 import torch
 
 __all__ = [
-    "conv3x3_min_tanh2", "conv3x3_mul_lrelu_gelu", "conv3x3_scale_min",
-    "conv3x3_gn_scale_pool_clamp", "gn_workspace_bytes", "library_path",
-    "version", "X3Error", "load_library", "EXPORTED_SYMBOLS",
+    "conv3x3_min_tanh2", "conv3x3_mul_lrelu_gelu", "conv3x3_mul_lrelu_gelu_tanh",
+    "conv3x3_scale_min", "conv3x3_gn_scale_pool_clamp", "gn_workspace_bytes",
+    "conv3x3_bias", "epi_min_tanh2", "epi_scale_min", "epi_mul_lrelu_gelu",
+    "epi_mul_lrelu_gelu_tanh", "epi_gn_scale_pool_clamp",
+    "library_path", "version", "X3Error", "load_library", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,9 +28,12 @@ _lib = None
 
 EXPORTED_SYMBOLS = (
     "x3_conv3x3_min_tanh2_f32", "x3_conv3x3_mul_lrelu_gelu_f32",
+    "x3_conv3x3_mul_lrelu_gelu_tanh_f32", "x3_conv3x3_bias_f32",
     "x3_conv3x3_scale_min_f32", "x3_conv3x3_gn_workspace_bytes",
-    "x3_conv3x3_gn_scale_pool_clamp_f32", "x3_status_str", "x3_last_error",
-    "x3_version",
+    "x3_conv3x3_gn_scale_pool_clamp_f32",
+    "x3_epi_min_tanh2_f32", "x3_epi_scale_min_f32", "x3_epi_mul_lrelu_gelu_f32",
+    "x3_epi_mul_lrelu_gelu_tanh_f32", "x3_epi_gn_scale_pool_clamp_f32",
+    "x3_status_str", "x3_last_error", "x3_version",
 )
 
 STATUS_NAMES = {0: "X3_OK", 1: "X3_EINVAL", 2: "X3_ESHAPE", 3: "X3_EUNSUPPORTED",
@@ -61,14 +66,22 @@ def load_library():
     vp, f, i, sz = ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
     lib.x3_conv3x3_min_tanh2_f32.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.x3_conv3x3_mul_lrelu_gelu_f32.argtypes = [vp, vp, vp, vp, f, vp, i, i, i, i, i, vp]
+    lib.x3_conv3x3_mul_lrelu_gelu_tanh_f32.argtypes = [vp, vp, vp, vp, f, vp, i, i, i, i, i, vp]
+    lib.x3_conv3x3_bias_f32.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.x3_epi_min_tanh2_f32.argtypes = [vp, vp, i, i, i, i, vp]
+    lib.x3_epi_scale_min_f32.argtypes = [vp, f, vp, i, i, i, i, vp]
+    lib.x3_epi_mul_lrelu_gelu_f32.argtypes = [vp, vp, f, vp, i, i, i, i, vp]
+    lib.x3_epi_mul_lrelu_gelu_tanh_f32.argtypes = [vp, vp, f, vp, i, i, i, i, vp]
+    lib.x3_epi_gn_scale_pool_clamp_f32.argtypes = [
+        vp, vp, vp, vp, i, f, i, f, f, vp, i, i, i, i, vp]
     lib.x3_conv3x3_scale_min_f32.argtypes = [vp, vp, vp, f, vp, i, i, i, i, i, vp]
     lib.x3_conv3x3_gn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.x3_conv3x3_gn_workspace_bytes.restype = sz
     lib.x3_conv3x3_gn_scale_pool_clamp_f32.argtypes = [
         vp, vp, vp, vp, vp, vp, i, f, i, f, f, vp, vp, sz, i, i, i, i, i, vp]
-    for name in ("x3_conv3x3_min_tanh2_f32", "x3_conv3x3_mul_lrelu_gelu_f32",
-                 "x3_conv3x3_scale_min_f32", "x3_conv3x3_gn_scale_pool_clamp_f32"):
-        getattr(lib, name).restype = i
+    for name in EXPORTED_SYMBOLS:
+        if name.endswith("_f32"):
+            getattr(lib, name).restype = i
     lib.x3_status_str.argtypes = [i]
     lib.x3_status_str.restype = ctypes.c_char_p
     lib.x3_last_error.argtypes = []
@@ -168,6 +181,29 @@ def conv3x3_mul_lrelu_gelu(x, weight, bias, multiplier, neg_slope=0.01,
     return out
 
 
+def conv3x3_mul_lrelu_gelu_tanh(x, weight, bias, multiplier, neg_slope=0.01,
+                                out=None) -> torch.Tensor:
+    """gelu_tanh(leaky_relu((conv3x3(x) + bias) * multiplier[c])), [B,Cout,H-2,W-2]."""
+    lib = load_library()
+    x, w, b, B, Cin, H, W, Cout = _conv_inputs(x, weight, bias)
+    m = _vec(multiplier, "multiplier", Cout)
+    out = _out(out, (B, Cout, max(H - 2, 0), max(W - 2, 0)), x)
+    _check("x3_conv3x3_mul_lrelu_gelu_tanh_f32", lib.x3_conv3x3_mul_lrelu_gelu_tanh_f32(
+        _ptr(x), _ptr(w), _ptr(b), _ptr(m), float(neg_slope), _ptr(out),
+        B, Cin, H, W, Cout, _stream(x.device)))
+    return out
+
+
+def conv3x3_bias(x, weight, bias, out=None) -> torch.Tensor:
+    """conv3x3(x) + bias (valid, stride 1), [B,Cout,H-2,W-2]."""
+    lib = load_library()
+    x, w, b, B, Cin, H, W, Cout = _conv_inputs(x, weight, bias)
+    out = _out(out, (B, Cout, max(H - 2, 0), max(W - 2, 0)), x)
+    _check("x3_conv3x3_bias_f32", lib.x3_conv3x3_bias_f32(
+        _ptr(x), _ptr(w), _ptr(b), _ptr(out), B, Cin, H, W, Cout, _stream(x.device)))
+    return out
+
+
 def conv3x3_scale_min(x, weight, bias, scale=2.0, out=None) -> torch.Tensor:
     """min over output channels of (scale * (conv3x3(x) + bias)), [B,1,H-2,W-2]."""
     lib = load_library()
@@ -208,4 +244,71 @@ def conv3x3_gn_scale_pool_clamp(x, weight, bias, gamma, beta, scale, groups=16,
         _ptr(x), _ptr(w), _ptr(b), _ptr(g), _ptr(be), _ptr(s), int(groups), float(eps), k,
         float(lo), float(hi), _ptr(out), _ptr(workspace), ws_bytes, B, Cin, H, W, Cout,
         _stream(x.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Standalone epilogues over a stored conv output y [B, C, H, W]
+
+
+def _y(y):
+    y = _tensor(y, "y", 4)
+    return (y, *y.shape)
+
+
+def epi_min_tanh2(y, out=None) -> torch.Tensor:
+    """tanh(tanh(min over channels of y)), [B,1,H,W]."""
+    lib = load_library()
+    y, B, C, H, W = _y(y)
+    out = _out(out, (B, 1, H, W), y)
+    _check("x3_epi_min_tanh2_f32", lib.x3_epi_min_tanh2_f32(
+        _ptr(y), _ptr(out), B, C, H, W, _stream(y.device)))
+    return out
+
+
+def epi_scale_min(y, scale=2.0, out=None) -> torch.Tensor:
+    """min over channels of (scale * y), [B,1,H,W]."""
+    lib = load_library()
+    y, B, C, H, W = _y(y)
+    out = _out(out, (B, 1, H, W), y)
+    _check("x3_epi_scale_min_f32", lib.x3_epi_scale_min_f32(
+        _ptr(y), float(scale), _ptr(out), B, C, H, W, _stream(y.device)))
+    return out
+
+
+def _epi_gelu(name, y, multiplier, neg_slope, out):
+    lib = load_library()
+    y, B, C, H, W = _y(y)
+    m = _vec(multiplier, "multiplier", C)
+    out = _out(out, (B, C, H, W), y)
+    _check(name, getattr(lib, name)(_ptr(y), _ptr(m), float(neg_slope), _ptr(out),
+                                    B, C, H, W, _stream(y.device)))
+    return out
+
+
+def epi_mul_lrelu_gelu(y, multiplier, neg_slope=0.01, out=None) -> torch.Tensor:
+    """gelu_erf(leaky_relu(y * multiplier[c])); out may be y (in place)."""
+    return _epi_gelu("x3_epi_mul_lrelu_gelu_f32", y, multiplier, neg_slope, out)
+
+
+def epi_mul_lrelu_gelu_tanh(y, multiplier, neg_slope=0.01, out=None) -> torch.Tensor:
+    """gelu_tanh(leaky_relu(y * multiplier[c])); out may be y (in place)."""
+    return _epi_gelu("x3_epi_mul_lrelu_gelu_tanh_f32", y, multiplier, neg_slope, out)
+
+
+def epi_gn_scale_pool_clamp(y, gamma, beta, scale, groups=16, eps=1e-5, pool_k=4,
+                            lo=0.0, hi=1.0, out=None) -> torch.Tensor:
+    """clamp(maxpool_k(GroupNorm(y) * scale[c]), lo, hi), [B,C,Ph,Pw]."""
+    lib = load_library()
+    y, B, C, H, W = _y(y)
+    g = _vec(gamma, "gamma", C)
+    be = _vec(beta, "beta", C)
+    s = _vec(scale, "scale", C)
+    k = int(pool_k)
+    Ph = (H - k) // k + 1 if (k > 0 and H >= k) else 0
+    Pw = (W - k) // k + 1 if (k > 0 and W >= k) else 0
+    out = _out(out, (B, C, Ph, Pw), y)
+    _check("x3_epi_gn_scale_pool_clamp_f32", lib.x3_epi_gn_scale_pool_clamp_f32(
+        _ptr(y), _ptr(g), _ptr(be), _ptr(s), int(groups), float(eps), k, float(lo),
+        float(hi), _ptr(out), B, C, H, W, _stream(y.device)))
     return out

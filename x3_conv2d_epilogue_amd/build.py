@@ -19,7 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["x3conv.hip", "epi_min_tanh2.hip", "epi_mul_lrelu_gelu.hip",
-           "epi_scale_min.hip", "epi_gn_pool.hip"]
+           "epi_mul_lrelu_gelu_tanh.hip", "epi_scale_min.hip", "epi_gn_pool.hip",
+           "epi_split.hip"]
 LIB = os.path.join(PKG, "libx3conv.so")
 ARCH = "gfx950"
 

@@ -49,6 +49,8 @@
 
 #include <type_traits>
 
+#include "epi_math.hpp"
+
 namespace x3 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -68,8 +70,10 @@ enum Epilogue : int {
   EPI_SCALE_MIN = 2,       // min_co(scale * y)
   EPI_GN_POOL = 3,         // GroupNorm partials per group of 4 channels
                            // + pooling-window extrema
-  EPI_GN_POOL_CH = 4       // GroupNorm partials per channel (any group
+  EPI_GN_POOL_CH = 4,      // GroupNorm partials per channel (any group
                            // size) + pooling-window extrema
+  EPI_STORE = 5,           // the conv output itself (split path)
+  EPI_MUL_LRELU_GELU_TANH = 6  // gelu_tanh(lrelu(y * mult[co]))
 };
 
 // Kernel arguments (plain values, passed by value).
@@ -78,10 +82,10 @@ struct ConvArgs {
   const float* w;
   const float* b;
   float* out;
-  const float* v0;  // mult (EPI_MUL_LRELU_GELU) | gamma (EPI_GN_POOL*)
+  const float* v0;  // mult (EPI_MUL_LRELU_GELU*) | gamma (EPI_GN_POOL*)
   const float* v1;  // beta  (EPI_GN_POOL*)
   const float* v2;  // scale (EPI_GN_POOL*)
-  float s0;         // neg_slope (EPI_MUL_LRELU_GELU) | scale (EPI_SCALE_MIN)
+  float s0;         // neg_slope (EPI_MUL_LRELU_GELU*) | scale (EPI_SCALE_MIN)
   float4* part;     // GroupNorm partials (EPI_GN_POOL*)
   int B, Cin, H, W, Cout;
   int Ho, Wo;
@@ -176,26 +180,6 @@ __device__ __forceinline__ void lds_load_x4(__amdgpu_buffer_rsrc_t r,
 
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
-}
-
-// erf for the exact-GELU epilogue, by formula 7.1.26 of Abramowitz and
-// Stegun, Handbook of Mathematical Functions: for x >= 0,
-//   erf(x) ~ 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
-//   t = 1 / (1 + p x),
-// with absolute error at most 1.5e-7; erf is odd.  Costs one reciprocal,
-// one exp2 and six FMAs.
-__device__ __forceinline__ float erf_as(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float q = 1.061405429f;
-  q = fmaf(q, t, -1.453152027f);
-  q = fmaf(q, t, 1.421413741f);
-  q = fmaf(q, t, -0.284496736f);
-  q = fmaf(q, t, 0.254829592f);
-  q *= t;
-  // exp(-x^2) = 2^(-x^2 * log2(e))
-  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-  return copysignf(fmaf(-q, e, 1.0f), x);
 }
 
 // DPP lane permutations (within rows of 16 lanes), applied to a float.
@@ -425,7 +409,8 @@ __global__ void __launch_bounds__(G::NTHR)
     float bv = pad, pv = 0.0f;
     if (real) {
       bv = a.b[co];
-      if constexpr (EPI == EPI_MUL_LRELU_GELU) pv = a.v0[co];
+      if constexpr (EPI == EPI_MUL_LRELU_GELU || EPI == EPI_MUL_LRELU_GELU_TANH)
+        pv = a.v0[co];
       if constexpr (EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH)
         pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : 0.0f;
     }
@@ -499,7 +484,8 @@ __global__ void __launch_bounds__(G::NTHR)
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y),
                                               o_rsrc, off, 0, 0);
       }
-    } else if constexpr (EPI == EPI_MUL_LRELU_GELU) {
+    } else if constexpr (EPI == EPI_MUL_LRELU_GELU ||
+                         EPI == EPI_MUL_LRELU_GELU_TANH || EPI == EPI_STORE) {
       const float slope = a.s0;
       // bounded stores into this sample's [Cout][Ho][Wo] block; an offset
       // with bit 31 set (pixel outside the output) is dropped
@@ -522,9 +508,11 @@ __global__ void __launch_bounds__(G::NTHR)
           const float mv = s_par[co];
 #pragma unroll
           for (int j = 0; j < G::NW; ++j) {
-            float v = acc[mt][j][i] * mv;
-            v = (v >= 0.0f) ? v : slope * v;
-            const float y = 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
+            float y = acc[mt][j][i];
+            if constexpr (EPI != EPI_STORE) {
+              const float v = lrelu(y * mv, slope);
+              y = (EPI == EPI_MUL_LRELU_GELU) ? gelu_erf(v) : gelu_tanh(v);
+            }
             // (OR, not add: nothing can clear the drop bit)
             const uint32_t off =
                 (((uint32_t)co * HoWo + pix_off[j]) << 2) | drop[j];

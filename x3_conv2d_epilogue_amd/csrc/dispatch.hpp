@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "conv3x3_igemm.hpp"
+#include "epilogue_kernels.hpp"
 #include "x3conv.h"
 
 namespace x3i {
@@ -105,6 +106,14 @@ x3_status dispatch(const x3::ConvArgs& a, hipStream_t st) {
 x3_status launch_min_tanh2(const x3::ConvArgs& a, hipStream_t st);
 x3_status launch_mul_lrelu_gelu(const x3::ConvArgs& a, hipStream_t st);
 x3_status launch_scale_min(const x3::ConvArgs& a, hipStream_t st);
+x3_status launch_mul_lrelu_gelu_tanh(const x3::ConvArgs& a, hipStream_t st);
+// Split path: the conv output as is, and the standalone epilogue kernels.
+x3_status launch_conv_store(const x3::ConvArgs& a, hipStream_t st);
+x3_status launch_epi_chan(x3::ChanArgs c, int mode, int64_t B, hipStream_t st);
+x3_status launch_epi_ew(x3::EwArgs e, bool tanh_form, int64_t planes,
+                        hipStream_t st);
+x3_status launch_epi_gn(const x3::GnPoolArgs& g, int64_t blocks,
+                        hipStream_t st);
 // GroupNorm path: the conv pass (partials + pooled extrema), then the
 // finalize pass over B*groups workgroups.
 x3_status launch_gn_pool(const x3::ConvArgs& a, hipStream_t st);

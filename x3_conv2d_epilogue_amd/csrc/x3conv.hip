@@ -131,16 +131,17 @@ X3_API x3_status x3_conv3x3_min_tanh2_f32(const float* x, const float* w,
   return x3i::launch_min_tanh2(base_args(x, w, b, out, s), (hipStream_t)stream);
 }
 
-X3_API x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
-                                               const float* b,
-                                               const float* mult,
-                                               float neg_slope, float* out,
-                                               int B, int Cin, int H, int W,
-                                               int Cout, void* stream) {
+namespace {
+// Shared by the exact and the tanh-approximation GELU entry points, and
+// (mult == nullptr, store_only) by the plain convolution.
+x3_status conv_elementwise(const float* x, const float* w, const float* b,
+                           const float* mult, float neg_slope, float* out,
+                           int B, int Cin, int H, int W, int Cout, void* stream,
+                           bool store_only, bool tanh_form) {
   Shape s;
   x3_status rc = check_common(x, w, b, out, B, Cin, H, W, Cout, s);
   if (rc != X3_OK) return rc;
-  if (!mult) return fail(X3_EINVAL, "null multiplier pointer");
+  if (!store_only && !mult) return fail(X3_EINVAL, "null multiplier pointer");
   // (channels padded to whole channel blocks must stay addressable too)
   if ((uint64_t)x3i::padded_cout(Cout) * (H - 2) * (W - 2) * 4 >= (1ull << 31))
     return fail(X3_EUNSUPPORTED, "one sample of out must be smaller than 2 GiB");
@@ -154,7 +155,35 @@ X3_API x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
   x3::ConvArgs a = base_args(x, w, b, out, s);
   a.v0 = mult;
   a.s0 = neg_slope;
-  return x3i::launch_mul_lrelu_gelu(a, (hipStream_t)stream);
+  if (store_only) return x3i::launch_conv_store(a, (hipStream_t)stream);
+  return tanh_form ? x3i::launch_mul_lrelu_gelu_tanh(a, (hipStream_t)stream)
+                   : x3i::launch_mul_lrelu_gelu(a, (hipStream_t)stream);
+}
+}  // namespace
+
+X3_API x3_status x3_conv3x3_bias_f32(const float* x, const float* w,
+                                     const float* b, float* y, int B, int Cin,
+                                     int H, int W, int Cout, void* stream) {
+  return conv_elementwise(x, w, b, nullptr, 0.0f, y, B, Cin, H, W, Cout,
+                          stream, true, false);
+}
+
+X3_API x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
+                                               const float* b,
+                                               const float* mult,
+                                               float neg_slope, float* out,
+                                               int B, int Cin, int H, int W,
+                                               int Cout, void* stream) {
+  return conv_elementwise(x, w, b, mult, neg_slope, out, B, Cin, H, W, Cout,
+                          stream, false, false);
+}
+
+X3_API x3_status x3_conv3x3_mul_lrelu_gelu_tanh_f32(
+    const float* x, const float* w, const float* b, const float* mult,
+    float neg_slope, float* out, int B, int Cin, int H, int W, int Cout,
+    void* stream) {
+  return conv_elementwise(x, w, b, mult, neg_slope, out, B, Cin, H, W, Cout,
+                          stream, false, true);
 }
 
 X3_API x3_status x3_conv3x3_scale_min_f32(const float* x, const float* w,
@@ -176,6 +205,15 @@ X3_API x3_status x3_conv3x3_scale_min_f32(const float* x, const float* w,
 }
 
 namespace {
+// Workspace of the GroupNorm entry point: the statistics partials of the
+// fused kernel (pool 4), or the whole conv output (other windows).
+size_t gn_workspace(const Shape& s, int groups, int pool_k) {
+  if (pool_k != 4) return (size_t)s.B * s.Cout * s.Ho * s.Wo * sizeof(float);
+  return (size_t)s.B * groups *
+         x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups) *
+         sizeof(float4);
+}
+
 x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
                    int pool_k, Shape& s) {
   if (B < 0 || Cin < 1 || H < 1 || W < 1 || Cout < 1)
@@ -191,8 +229,6 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
                 H - 2, W - 2);
   if (Cout > x3::kMaxCout)
     return fail(X3_EUNSUPPORTED, "Cout=%d exceeds %d", Cout, x3::kMaxCout);
-  if (pool_k != 4)
-    return fail(X3_EUNSUPPORTED, "pool_k=%d not compiled in (4)", pool_k);
   if ((uint64_t)Cin * H * W * 4 >= (1ull << 31))
     return fail(X3_EUNSUPPORTED, "one sample of x must be smaller than 2 GiB");
   // (the kernel works in 64-channel blocks: padded channels and groups
@@ -203,10 +239,15 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
   const uint64_t cpad = (uint64_t)(Cout + 63) / 64 * 64;
   const uint64_t prows =
       x3i::gn_partials_per_channel(Cout, groups) ? cpad : cpad / 4;
-  if (cpad * P * 4 >= (1ull << 31) ||
-      prows * x3i::gn_pps(H - 2, W - 2, Cin, Cout) * 16 >= (1ull << 31))
+  if (pool_k == 4 &&
+      (cpad * P * 4 >= (1ull << 31) ||
+       prows * x3i::gn_pps(H - 2, W - 2, Cin, Cout) * 16 >= (1ull << 31)))
     return fail(X3_EUNSUPPORTED,
                 "one sample of out or of the workspace must be < 2 GiB");
+  // other windows take the split path: the conv output is stored whole
+  if (pool_k != 4 && (uint64_t)x3i::padded_cout(Cout) * (H - 2) * (W - 2) * 4 >=
+                         (1ull << 31))
+    return fail(X3_EUNSUPPORTED, "one sample of the conv output must be < 2 GiB");
   s = Shape{B, Cin, H, W, Cout, H - 2, W - 2};
   return X3_OK;
 }
@@ -220,9 +261,7 @@ X3_API size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W,
   const x3_status rc = check_gn(B, Cin, H, W, Cout, groups, pool_k, s);
   __builtin_memcpy(g_err, saved, sizeof(g_err));
   if (rc != X3_OK) return 0;
-  return (size_t)B * groups *
-         x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups) *
-         sizeof(float4);
+  return gn_workspace(s, groups, pool_k);
 }
 
 X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
@@ -242,9 +281,7 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   if (!std::isfinite(lo) || !std::isfinite(hi) || lo > hi)
     return fail(X3_EINVAL, "clamp bounds must be finite with lo <= hi");
   if (B == 0) return X3_OK;
-  const size_t need =
-      (size_t)B * groups *
-      x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups) * sizeof(float4);
+  const size_t need = gn_workspace(s, groups, pool_k);
   if (!workspace || workspace_bytes < need)
     return fail(X3_EWORKSPACE, "workspace of %zu bytes needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -262,6 +299,29 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
     return fail(X3_EINVAL, "out or workspace overlaps another buffer");
 
   hipStream_t st = (hipStream_t)stream;
+  if (pool_k != 4) {
+    // split path: conv output into the workspace, then the standalone
+    // GroupNorm -> scale -> pool -> clamp kernel
+    rc = x3i::launch_conv_store(base_args(x, w, b, (float*)workspace, s), st);
+    if (rc != X3_OK) return rc;
+    x3::GnPoolArgs g{};
+    g.y = (const float*)workspace;
+    g.gamma = gamma;
+    g.beta = beta;
+    g.scale = scale;
+    g.out = out;
+    g.groups = groups;
+    g.cpg = Cout / groups;
+    g.H = s.Ho;
+    g.W = s.Wo;
+    g.k = pool_k;
+    g.Ph = Ph;
+    g.Pw = Pw;
+    g.eps = eps;
+    g.lo = lo;
+    g.hi = hi;
+    return x3i::launch_epi_gn(g, (int64_t)B * groups, st);
+  }
   x3::ConvArgs a = base_args(x, w, b, out, s);
   a.v0 = gamma;
   a.v1 = beta;
@@ -288,6 +348,141 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   f.hi = hi;
   f.count = (double)f.cpg * s.Ho * s.Wo;
   return x3i::launch_gn_finalize(f, B * groups, st);
+}
+
+// ============================================================================
+// Standalone epilogues over a stored conv output y [B][C][H][W]
+
+namespace {
+// Checks shared by the standalone epilogues.  `out_bytes` is the size of
+// the output; inputs are y and the per-channel vectors given.
+x3_status check_epi(const float* y, const float* out, int B, int C, int H,
+                    int W) {
+  g_err[0] = '\0';
+  if (B < 0 || C < 1 || H < 1 || W < 1)
+    return fail(X3_EINVAL, "sizes must be positive (B >= 0): B=%d C=%d H=%d W=%d",
+                B, C, H, W);
+  if (B > 0 && (!y || !out)) return fail(X3_EINVAL, "null y or out pointer");
+  return X3_OK;
+}
+}  // namespace
+
+X3_API x3_status x3_epi_min_tanh2_f32(const float* y, float* out, int B, int C,
+                                      int H, int W, void* stream) {
+  x3_status rc = check_epi(y, out, B, C, H, W);
+  if (rc != X3_OK || B == 0) return rc;
+  const int64_t P = (int64_t)H * W;
+  if (overlaps(out, (size_t)B * P * 4, y, (size_t)B * C * P * 4))
+    return fail(X3_EINVAL, "out overlaps y");
+  x3::ChanArgs c{};
+  c.y = y;
+  c.out = out;
+  c.C = C;
+  c.P = P;
+  return x3i::launch_epi_chan(c, x3::CHAN_MIN_TANH2, B, (hipStream_t)stream);
+}
+
+X3_API x3_status x3_epi_scale_min_f32(const float* y, float scale, float* out,
+                                      int B, int C, int H, int W,
+                                      void* stream) {
+  x3_status rc = check_epi(y, out, B, C, H, W);
+  if (rc != X3_OK) return rc;
+  if (!std::isfinite(scale)) return fail(X3_EINVAL, "scale must be finite");
+  if (B == 0) return X3_OK;
+  const int64_t P = (int64_t)H * W;
+  if (overlaps(out, (size_t)B * P * 4, y, (size_t)B * C * P * 4))
+    return fail(X3_EINVAL, "out overlaps y");
+  x3::ChanArgs c{};
+  c.y = y;
+  c.out = out;
+  c.C = C;
+  c.P = P;
+  c.scale = scale;
+  return x3i::launch_epi_chan(c, x3::CHAN_SCALE_MIN, B, (hipStream_t)stream);
+}
+
+namespace {
+x3_status epi_gelu(const float* y, const float* mult, float neg_slope,
+                   float* out, int B, int C, int H, int W, void* stream,
+                   bool tanh_form) {
+  x3_status rc = check_epi(y, out, B, C, H, W);
+  if (rc != X3_OK) return rc;
+  if (!mult) return fail(X3_EINVAL, "null multiplier pointer");
+  if (!std::isfinite(neg_slope))
+    return fail(X3_EINVAL, "neg_slope must be finite");
+  if (B == 0) return X3_OK;
+  const int64_t P = (int64_t)H * W;
+  const size_t nb = (size_t)B * C * P * 4;
+  // out may be y itself, but no other overlap
+  if ((out != y && overlaps(out, nb, y, nb)) || overlaps(out, nb, mult, (size_t)C * 4))
+    return fail(X3_EINVAL, "out partially overlaps y, or overlaps mult");
+  x3::EwArgs e{};
+  e.y = y;
+  e.mult = mult;
+  e.out = out;
+  e.C = C;
+  e.P = P;
+  e.slope = neg_slope;
+  return x3i::launch_epi_ew(e, tanh_form, (int64_t)B * C, (hipStream_t)stream);
+}
+}  // namespace
+
+X3_API x3_status x3_epi_mul_lrelu_gelu_f32(const float* y, const float* mult,
+                                           float neg_slope, float* out, int B,
+                                           int C, int H, int W, void* stream) {
+  return epi_gelu(y, mult, neg_slope, out, B, C, H, W, stream, false);
+}
+
+X3_API x3_status x3_epi_mul_lrelu_gelu_tanh_f32(const float* y,
+                                                const float* mult,
+                                                float neg_slope, float* out,
+                                                int B, int C, int H, int W,
+                                                void* stream) {
+  return epi_gelu(y, mult, neg_slope, out, B, C, H, W, stream, true);
+}
+
+X3_API x3_status x3_epi_gn_scale_pool_clamp_f32(
+    const float* y, const float* gamma, const float* beta, const float* scale,
+    int groups, float eps, int pool_k, float lo, float hi, float* out, int B,
+    int C, int H, int W, void* stream) {
+  x3_status rc = check_epi(y, out, B, C, H, W);
+  if (rc != X3_OK) return rc;
+  if (groups < 1) return fail(X3_EINVAL, "groups must be >= 1");
+  if (pool_k < 1) return fail(X3_EINVAL, "pool_k must be >= 1");
+  if (C % groups != 0)
+    return fail(X3_ESHAPE, "C=%d is not divisible by groups=%d", C, groups);
+  if (H < pool_k || W < pool_k)
+    return fail(X3_ESHAPE, "input %dx%d is smaller than the pool window", H, W);
+  if (!gamma || !beta || !scale)
+    return fail(X3_EINVAL, "null gamma/beta/scale pointer");
+  if (!(eps > 0.0f) || !std::isfinite(eps))
+    return fail(X3_EINVAL, "eps must be positive and finite");
+  if (!std::isfinite(lo) || !std::isfinite(hi) || lo > hi)
+    return fail(X3_EINVAL, "clamp bounds must be finite with lo <= hi");
+  if (B == 0) return X3_OK;
+  const int Ph = (H - pool_k) / pool_k + 1, Pw = (W - pool_k) / pool_k + 1;
+  const size_t ob = (size_t)B * C * Ph * Pw * 4, cb = (size_t)C * 4;
+  if (overlaps(out, ob, y, (size_t)B * C * H * W * 4) ||
+      overlaps(out, ob, gamma, cb) || overlaps(out, ob, beta, cb) ||
+      overlaps(out, ob, scale, cb))
+    return fail(X3_EINVAL, "out overlaps an input");
+  x3::GnPoolArgs g{};
+  g.y = y;
+  g.gamma = gamma;
+  g.beta = beta;
+  g.scale = scale;
+  g.out = out;
+  g.groups = groups;
+  g.cpg = C / groups;
+  g.H = H;
+  g.W = W;
+  g.k = pool_k;
+  g.Ph = Ph;
+  g.Pw = Pw;
+  g.eps = eps;
+  g.lo = lo;
+  g.hi = hi;
+  return x3i::launch_epi_gn(g, (int64_t)B * groups, (hipStream_t)stream);
 }
 
 X3_API const char* x3_status_str(x3_status s) {
