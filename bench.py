@@ -86,6 +86,58 @@ def make_op(x3, wl, g, out=None, workspace=None):
     raise ValueError(wl.op)
 
 
+def split_ops(x3, wl, g, y, out):
+    """The unfused form of a workload: (conv op writing y, epilogue op on y)."""
+    p = wl.params
+    conv = lambda: x3.conv3x3_bias(g["x"], g["weight"], g["bias"], out=y)  # noqa: E731
+    if wl.op == "min_tanh2":
+        epi = lambda: x3.epi_min_tanh2(y, out=out)  # noqa: E731
+    elif wl.op == "scale_min":
+        epi = lambda: x3.epi_scale_min(y, p["scale"], out=out)  # noqa: E731
+    elif wl.op == "mul_lrelu_gelu":
+        epi = lambda: x3.epi_mul_lrelu_gelu(y, g["multiplier"], p["neg_slope"], out=out)  # noqa: E731
+    else:
+        import torch  # noqa: PLC0415
+        ws = torch.empty(x3.load_library().x3_epi_gn_workspace_bytes(wl.B, wl.Cout),
+                         dtype=torch.uint8, device=y.device)
+        epi = lambda: x3.epi_gn_scale_pool_clamp(  # noqa: E731
+            y, g["gamma"], g["beta"], g["scale"], p["groups"], p["eps"], p["pool_k"], p["lo"],
+            p["hi"], out=out, workspace=ws)
+    return conv, epi
+
+
+def epilogue_bytes(wl) -> int:
+    """Algorithmic HBM bytes of a standalone epilogue: y read once, the
+    output written once, per-channel vectors read once."""
+    y = wl.B * wl.Cout * wl.Ho * wl.Wo
+    n_out = 1
+    for d in out_shape(wl):
+        n_out *= d
+    n_par = {"mul_lrelu_gelu": wl.Cout, "gn_scale_pool_clamp": 3 * wl.Cout}.get(wl.op, 0)
+    return 4 * (y + n_out + n_par)
+
+
+def ablation(torch, x3, wl, dev, steps, warmup, fused_ms):
+    """Time the split path (conv storing y, then the standalone epilogue)
+    against the fused kernel on the same workload."""
+    g = gpu_inputs(torch, wl, dev, seed=0)
+    y = torch.empty((wl.B, wl.Cout, wl.Ho, wl.Wo), device=dev)
+    out = torch.empty(out_shape(wl), device=dev)
+    conv, epi = split_ops(x3, wl, g, y, out)
+    _, conv_ms = time_op(torch, conv, steps, warmup)
+    _, epi_ms = time_op(torch, epi, steps, warmup)
+    _, split_ms = time_op(torch, lambda: (conv(), epi()), steps, warmup)
+    eb = epilogue_bytes(wl)
+    gbps = eb / (epi_ms * 1e-3) / 1e9
+    del g, y, out
+    torch.cuda.empty_cache()
+    return {"fused_kernel_ms": round(fused_ms, 4), "conv_store_ms": round(conv_ms, 4),
+            "epilogue_ms": round(epi_ms, 4), "split_ms": round(split_ms, 4),
+            "fused_speedup": round(split_ms / fused_ms, 3),
+            "epilogue_bytes": eb, "epilogue_GBps": round(gbps, 1),
+            "epilogue_frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def out_shape(wl):
     if wl.op in ("min_tanh2", "scale_min"):
         return (wl.B, 1, wl.Ho, wl.Wo)
@@ -193,6 +245,8 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-others", action="store_true",
                     help="do not time the other four workloads")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the unfused (conv + standalone epilogue) comparison")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -283,6 +337,19 @@ def main():
     if wl.op == "gn_scale_pool_clamp":
         roof["note"] = "two kernels per launch (conv pass + finalize); kernel_ms covers both"
 
+    # Unfused comparison: the same conv storing its output, then the
+    # standalone epilogue kernel, per workload (after the headline timing).
+    abl = {}
+    if not args.no_ablation:
+        fused = {args.workload: ms_kernel}
+        fused.update({k: v["kernel_ms"] for k, v in others.items()})
+        for name in WORKLOAD_ORDER:
+            if name not in fused or WORKLOADS[name].B * WORKLOADS[name].Cout < 1024:
+                continue  # (the tiny case says nothing about bandwidth)
+            log(f"ablation {name}: conv + standalone epilogue")
+            abl[name] = ablation(torch, x3, WORKLOADS[name], dev, max(3, min(args.steps, 20)),
+                                 max(1, min(args.warmup, 5)), fused[name])
+
     cpu = None
     parity = None
     if args.cpu_budget > 0:
@@ -311,6 +378,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "other_workloads": others,
+        "unfused_ablation": abl,
         "host": {"cpu": platform.processor() or platform.machine(), "cpu_count": os.cpu_count(),
                  "device": torch.cuda.get_device_name(0)},
     }

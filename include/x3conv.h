@@ -131,8 +131,8 @@ size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W, int Cout,
  * pool_k == 4 the conv kernel writes statistics partials (workspace) and
  * the window extrema (out), then a finalize normalizes out in place.  Any
  * other pool_k takes the split path: the conv output goes to the workspace
- * (B*Cout*Ho*Wo floats), then x3_epi_gn_scale_pool_clamp_f32's kernel runs
- * on it.
+ * (B*Cout*Ho*Wo floats, then B*Cout 16-byte partials at the next 256-byte
+ * boundary), then x3_epi_gn_scale_pool_clamp_f32's kernels run on it.
  * Supported: any groups dividing Cout (Cout <= 1024), any pool_k >= 1;
  * eps > 0 and finite lo <= hi (else X3_EINVAL); Ho, Wo >= pool_k (else
  * X3_ESHAPE). */
@@ -172,18 +172,26 @@ x3_status x3_epi_mul_lrelu_gelu_tanh_f32(const float* y, const float* mult,
                                          float neg_slope, float* out, int B,
                                          int C, int H, int W, void* stream);
 
+/* Bytes of device workspace x3_epi_gn_scale_pool_clamp_f32 needs: one
+ * 16-byte partial per (sample, channel) plane (0 for invalid sizes). */
+size_t x3_epi_gn_workspace_bytes(int B, int C);
+
 /* [P85]: GroupNorm(groups, eps, gamma, beta) -> * scale[c] ->
  * MaxPool2d(pool_k, stride pool_k, floor) -> clamp[lo, hi], as
  * x3_conv3x3_gn_scale_pool_clamp_f32 defines it, on y.  out [B][C][Ph][Pw],
  * Ph = (H - pool_k) / pool_k + 1, Pw likewise.  groups must divide C and
  * H, W >= pool_k (else X3_ESHAPE); eps > 0, finite lo <= hi (else
- * X3_EINVAL).  No workspace: one workgroup per (sample, group) computes the
- * statistics and then the group's pooled outputs. */
+ * X3_EINVAL).  workspace: at least x3_epi_gn_workspace_bytes(B, C) bytes,
+ * 16-byte aligned, caller-owned, overwritten (else X3_EWORKSPACE /
+ * X3_EINVAL).  Two kernels: per-plane statistics + window extrema (parked
+ * in out), then the per-group finalize. */
 x3_status x3_epi_gn_scale_pool_clamp_f32(const float* y, const float* gamma,
                                          const float* beta, const float* scale,
                                          int groups, float eps, int pool_k,
-                                         float lo, float hi, float* out, int B,
-                                         int C, int H, int W, void* stream);
+                                         float lo, float hi, float* out,
+                                         void* workspace,
+                                         size_t workspace_bytes, int B, int C,
+                                         int H, int W, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* x3_status_str(x3_status s);

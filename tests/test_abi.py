@@ -126,8 +126,10 @@ def test_gn_workspace_bytes(lib):
     # one group of all 64 channels
     assert f(2, 8, 128, 128, 64, 1, 4) == 2 * 1 * 64 * 128 * 16
     # other pool windows take the split path: the workspace holds the conv
-    # output, [2, 64, 126, 126] floats
-    assert f(2, 8, 128, 128, 64, 16, 3) == 2 * 64 * 126 * 126 * 4
+    # output, [2, 64, 126, 126] floats, then 2 * 64 plane partials of 16 B at
+    # the next 256-byte boundary
+    y_bytes = (2 * 64 * 126 * 126 * 4 + 255) // 256 * 256
+    assert f(2, 8, 128, 128, 64, 16, 3) == y_bytes + 2 * 64 * 16
     assert f(2, 8, 128, 128, 64, 16, 0) == 0   # pool 0: invalid
     assert f(2, 8, 5, 5, 64, 16, 4) == 0       # 3x3 conv output < pool window
     assert f(2, 8, 128, 128, 1028, 257, 4) == 0  # Cout above 1024
@@ -214,14 +216,16 @@ def test_standalone_epilogue_validation(lib):
         assert f(Y, M, 0.01, fake(0x10000010), 2, 4, 8, 8, s) == EINVAL
         assert f(None, M, 0.01, None, 0, 4, 8, 8, s) == OK
     f = lib.x3_epi_gn_scale_pool_clamp_f32
-    G_, BE, SC = M, fake(0x51000000), fake(0x52000000)
+    G_, BE, SC, WS = M, fake(0x51000000), fake(0x52000000), fake(0x60000000)
+    assert lib.x3_epi_gn_workspace_bytes(2, 16) == 2 * 16 * 16
+    assert lib.x3_epi_gn_workspace_bytes(2, 0) == 0
 
     def call(**kw):
         a = dict(y=Y, g=G_, be=BE, sc=SC, groups=4, eps=1e-5, k=4, lo=0.0, hi=1.0, out=O,
-                 B=2, C=16, H=32, W=32)
+                 ws=WS, wsb=2 * 16 * 16, B=2, C=16, H=32, W=32)
         a.update(kw)
         return f(a["y"], a["g"], a["be"], a["sc"], a["groups"], a["eps"], a["k"], a["lo"],
-                 a["hi"], a["out"], a["B"], a["C"], a["H"], a["W"], s)
+                 a["hi"], a["out"], a["ws"], a["wsb"], a["B"], a["C"], a["H"], a["W"], s)
 
     assert call(groups=0) == EINVAL
     assert call(k=0) == EINVAL
@@ -231,4 +235,8 @@ def test_standalone_epilogue_validation(lib):
     assert call(lo=2.0) == EINVAL
     assert call(sc=None) == EINVAL
     assert call(out=Y) == EINVAL
+    assert call(ws=None) == EWS
+    assert call(wsb=2 * 16 * 16 - 1) == EWS
+    assert call(ws=fake(0x60000008)) == EINVAL   # misaligned workspace
+    assert call(ws=O) == EINVAL                  # workspace overlaps out
     assert call(B=0, y=None, out=None) == OK

@@ -32,7 +32,8 @@ EXPORTED_SYMBOLS = (
     "x3_conv3x3_scale_min_f32", "x3_conv3x3_gn_workspace_bytes",
     "x3_conv3x3_gn_scale_pool_clamp_f32",
     "x3_epi_min_tanh2_f32", "x3_epi_scale_min_f32", "x3_epi_mul_lrelu_gelu_f32",
-    "x3_epi_mul_lrelu_gelu_tanh_f32", "x3_epi_gn_scale_pool_clamp_f32",
+    "x3_epi_mul_lrelu_gelu_tanh_f32", "x3_epi_gn_workspace_bytes",
+    "x3_epi_gn_scale_pool_clamp_f32",
     "x3_status_str", "x3_last_error", "x3_version",
 )
 
@@ -72,8 +73,10 @@ def load_library():
     lib.x3_epi_scale_min_f32.argtypes = [vp, f, vp, i, i, i, i, vp]
     lib.x3_epi_mul_lrelu_gelu_f32.argtypes = [vp, vp, f, vp, i, i, i, i, vp]
     lib.x3_epi_mul_lrelu_gelu_tanh_f32.argtypes = [vp, vp, f, vp, i, i, i, i, vp]
+    lib.x3_epi_gn_workspace_bytes.argtypes = [i, i]
+    lib.x3_epi_gn_workspace_bytes.restype = sz
     lib.x3_epi_gn_scale_pool_clamp_f32.argtypes = [
-        vp, vp, vp, vp, i, f, i, f, f, vp, i, i, i, i, vp]
+        vp, vp, vp, vp, i, f, i, f, f, vp, vp, sz, i, i, i, i, vp]
     lib.x3_conv3x3_scale_min_f32.argtypes = [vp, vp, vp, f, vp, i, i, i, i, i, vp]
     lib.x3_conv3x3_gn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.x3_conv3x3_gn_workspace_bytes.restype = sz
@@ -297,7 +300,7 @@ def epi_mul_lrelu_gelu_tanh(y, multiplier, neg_slope=0.01, out=None) -> torch.Te
 
 
 def epi_gn_scale_pool_clamp(y, gamma, beta, scale, groups=16, eps=1e-5, pool_k=4,
-                            lo=0.0, hi=1.0, out=None) -> torch.Tensor:
+                            lo=0.0, hi=1.0, out=None, workspace=None) -> torch.Tensor:
     """clamp(maxpool_k(GroupNorm(y) * scale[c]), lo, hi), [B,C,Ph,Pw]."""
     lib = load_library()
     y, B, C, H, W = _y(y)
@@ -308,7 +311,13 @@ def epi_gn_scale_pool_clamp(y, gamma, beta, scale, groups=16, eps=1e-5, pool_k=4
     Ph = (H - k) // k + 1 if (k > 0 and H >= k) else 0
     Pw = (W - k) // k + 1 if (k > 0 and W >= k) else 0
     out = _out(out, (B, C, Ph, Pw), y)
+    need = int(lib.x3_epi_gn_workspace_bytes(B, C))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=y.device)
+    if workspace.device != y.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on y's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check("x3_epi_gn_scale_pool_clamp_f32", lib.x3_epi_gn_scale_pool_clamp_f32(
         _ptr(y), _ptr(g), _ptr(be), _ptr(s), int(groups), float(eps), k, float(lo),
-        float(hi), _ptr(out), B, C, H, W, _stream(y.device)))
+        float(hi), _ptr(out), _ptr(workspace), ws_bytes, B, C, H, W, _stream(y.device)))
     return out

@@ -112,7 +112,9 @@ x3_status launch_conv_store(const x3::ConvArgs& a, hipStream_t st);
 x3_status launch_epi_chan(x3::ChanArgs c, int mode, int64_t B, hipStream_t st);
 x3_status launch_epi_ew(x3::EwArgs e, bool tanh_form, int64_t planes,
                         hipStream_t st);
-x3_status launch_epi_gn(const x3::GnPoolArgs& g, int64_t blocks,
+// (the plane kernel, then the finalize; g.part holds B*C float4)
+x3_status launch_epi_gn(const x3::GnPlaneArgs& g, int64_t B, int groups,
+                        const float* beta, float eps, float lo, float hi,
                         hipStream_t st);
 // GroupNorm path: the conv pass (partials + pooled extrema), then the
 // finalize pass over B*groups workgroups.

@@ -67,16 +67,36 @@ x3_status launch_epi_ew(x3::EwArgs e, bool tanh_form, int64_t planes,
   return launched("elementwise epilogue kernel");
 }
 
-x3_status launch_epi_gn(const x3::GnPoolArgs& g, int64_t blocks, hipStream_t st) {
-  if (blocks >= (1ll << 31))
-    return fail(X3_EUNSUPPORTED, "too many (sample, group) pairs for one launch");
-  const int64_t total = (int64_t)g.cpg * g.H * g.W;
-  const dim3 grid((unsigned)blocks), block(x3::kEpiThreads);
-  if (total % 4 == 0 && aligned16(g.y))
-    hipLaunchKernelGGL((x3::gn_pool_kernel<true>), grid, block, 0, st, g);
+x3_status launch_epi_gn(const x3::GnPlaneArgs& g, int64_t B, int groups,
+                        const float* beta, float eps, float lo, float hi,
+                        hipStream_t st) {
+  const int64_t planes = B * g.C;
+  if (planes >= (1ll << 31) || B * groups >= (1ll << 31))
+    return fail(X3_EUNSUPPORTED, "too many planes for one launch");
+  const dim3 grid((unsigned)planes), block(x3::kEpiThreads);
+  if (g.k == 4)
+    hipLaunchKernelGGL((x3::gn_plane_kernel<4>), grid, block, 0, st, g);
   else
-    hipLaunchKernelGGL((x3::gn_pool_kernel<false>), grid, block, 0, st, g);
-  return launched("GroupNorm pooling kernel");
+    hipLaunchKernelGGL((x3::gn_plane_kernel<0>), grid, block, 0, st, g);
+  const x3_status rc = launched("GroupNorm plane kernel");
+  if (rc != X3_OK) return rc;
+  // the finalize of the fused path: merge each group's cpg plane partials,
+  // then normalize, scale and clamp the parked extrema in place
+  x3::GnFinArgs f{};
+  f.part = g.part;
+  f.gamma = g.gamma;
+  f.beta = beta;
+  f.scale = g.scale;
+  f.out = g.out;
+  f.groups = groups;
+  f.cpg = g.C / groups;
+  f.pps = f.cpg;
+  f.plane = g.Ph * g.Pw;
+  f.eps = eps;
+  f.lo = lo;
+  f.hi = hi;
+  f.count = (double)f.cpg * g.H * g.W;
+  return launch_gn_finalize(f, (int)(B * groups), st);
 }
 
 }  // namespace x3i

@@ -2,9 +2,9 @@
 // stored conv output y [B][C][H][W] (NCHW, fp32).  They serve the split
 // path: a caller's own convolution output, the unfused comparison against
 // the fused kernels, and pooling windows that the fused GroupNorm epilogue
-// does not cover.  All are bound by HBM bandwidth: y is read once (twice for
-// GroupNorm: statistics, then the pooled normalization, the second read
-// mostly from L2), with 16-byte loads where the layout allows.
+// does not cover.  Each reads y once, with 16-byte loads where the layout
+// allows, and is bound by HBM bandwidth (the GELU form by its arithmetic
+// nearly as much).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,6 +15,24 @@
 namespace x3 {
 
 constexpr int kEpiThreads = 256;
+
+// Streaming (non-temporal) 16-byte loads and stores: y is read once and the
+// outputs are not read back by these kernels, so neither should displace
+// cache lines that other traffic reuses.
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const nt_f32x4 v =
+      __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(float4 r, float4* p) {
+  nt_f32x4 v;
+  v.x = r.x;
+  v.y = r.y;
+  v.z = r.z;
+  v.w = r.w;
+  __builtin_nontemporal_store(v, reinterpret_cast<nt_f32x4*>(p));
+}
 
 // ---------------------------------------------------------------------------
 // Channel extremum: out[n][p] = tanh(tanh(min_c y[n][c][p])), or
@@ -39,7 +57,8 @@ __device__ __forceinline__ float chan_finish(float m, float scale) {
 }
 
 // One thread per pixel, or per 4 pixels with VEC (P % 4 == 0 and both
-// buffers 16-byte aligned).  The channel loop keeps 4 loads in flight.
+// buffers 16-byte aligned).  The channel loop keeps 8 (VEC) or 4 loads in
+// flight.
 template <int MODE, bool VEC>
 __global__ void __launch_bounds__(kEpiThreads) chan_extremum_kernel(const ChanArgs a) {
   const int64_t n = blockIdx.x / a.nchunk;
@@ -57,13 +76,17 @@ __global__ void __launch_bounds__(kEpiThreads) chan_extremum_kernel(const ChanAr
     const float4* src = reinterpret_cast<const float4*>(yn) + q;
     float4 m = src[0];
     int c = 1;
-    for (; c + 3 < a.C; c += 4) {
-      const float4 v0 = src[(c + 0) * nq], v1 = src[(c + 1) * nq];
-      const float4 v2 = src[(c + 2) * nq], v3 = src[(c + 3) * nq];
-      m.x = pick(pick(m.x, v0.x), pick(pick(v1.x, v2.x), v3.x));
-      m.y = pick(pick(m.y, v0.y), pick(pick(v1.y, v2.y), v3.y));
-      m.z = pick(pick(m.z, v0.z), pick(pick(v1.z, v2.z), v3.z));
-      m.w = pick(pick(m.w, v0.w), pick(pick(v1.w, v2.w), v3.w));
+    for (; c + 7 < a.C; c += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ld_stream(src + (c + u) * nq);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        m.x = pick(m.x, v[u].x);
+        m.y = pick(m.y, v[u].y);
+        m.z = pick(m.z, v[u].z);
+        m.w = pick(m.w, v[u].w);
+      }
     }
     for (; c < a.C; ++c) {
       const float4 v = src[c * nq];
@@ -130,7 +153,7 @@ __global__ void __launch_bounds__(kEpiThreads) mul_lrelu_gelu_kernel(const EwArg
 #pragma unroll
     for (int k = 0; k < kEwPerThread; ++k) {
       const int64_t q = first + k * kEpiThreads;
-      if (q < nq) v[k] = s4[q];
+      if (q < nq) v[k] = ld_stream(s4 + q);
     }
 #pragma unroll
     for (int k = 0; k < kEwPerThread; ++k) {
@@ -141,7 +164,7 @@ __global__ void __launch_bounds__(kEpiThreads) mul_lrelu_gelu_kernel(const EwArg
         r.y = ew_op<TANH>(v[k].y, m, a.slope);
         r.z = ew_op<TANH>(v[k].z, m, a.slope);
         r.w = ew_op<TANH>(v[k].w, m, a.slope);
-        d4[q] = r;
+        st_stream(r, d4 + q);
       }
     }
   } else {
@@ -160,23 +183,38 @@ __global__ void __launch_bounds__(kEpiThreads) mul_lrelu_gelu_kernel(const EwArg
 }
 
 // ---------------------------------------------------------------------------
-// GroupNorm -> per-channel scale -> MaxPool2d(k, stride k, floor) -> clamp.
-// One workgroup per (sample, group): the group's cpg channel planes are one
-// contiguous block of y.  Pass 1: count-free shifted sums in double about
-// K = the block's first element, giving mean = K + S1/N and
-// M2 = S2 - S1^2/N (biased variance M2/N).  Pass 2: every pooled output of
-// the group: the maximum over its k x k window of
-// z = ((y - mean) * rstd * gamma + beta) * scale, clamped to [lo, hi].
-struct GnPoolArgs {
+// GroupNorm -> per-channel scale -> MaxPool2d(k, stride k, floor) -> clamp
+// on a stored y, in one read of y: this kernel, one workgroup per (sample,
+// channel) plane, then the GroupNorm finalize of the fused path.
+//
+// The map z = (y - mean) * A + Bc (A = rstd*gamma*scale, Bc = beta*scale)
+// is monotone in y with the sign of A, so the window maximum of z is z of
+// the window maximum of y where gamma*scale >= 0 and of the window minimum
+// otherwise.  The plane kernel walks the pooling windows: every element
+// feeds the plane's statistics (sums of d = y - K and d^2 about K, the
+// plane's first element, per thread in fp32 over its few dozen elements,
+// then over the workgroup in double), and each window's raw extremum is
+// parked in out.  The elements outside every window (the floor-mode
+// remainder rows and columns) feed the statistics only.  The plane's
+// (sum, M2, count) goes to part[n][c]; the finalize merges the cpg partials
+// of a group and maps the parked extrema through z and the clamp.
+struct GnPlaneArgs {
   const float* y;
   const float* gamma;
-  const float* beta;
   const float* scale;
-  float* out;
-  int groups, cpg;
-  int H, W, k, Ph, Pw;
-  float eps, lo, hi;
+  float* out;    // [B][C][Ph][Pw] parked extrema
+  float4* part;  // [B][C] plane partials
+  int C, H, W, k, Ph, Pw;
 };
+
+// Quad permutation of a float (DPP quad_perm; 0xB1 swaps lanes 0<->1 and
+// 2<->3 of each quad, 0x4E swaps 0<->2 and 1<->3).
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                         0xF, 0xF, false));
+}
 
 template <int NT>
 __device__ __forceinline__ double block_sum_d(double v, double* red) {
@@ -190,57 +228,136 @@ __device__ __forceinline__ double block_sum_d(double v, double* red) {
   return t;
 }
 
-template <bool VEC>
-__global__ void __launch_bounds__(kEpiThreads) gn_pool_kernel(const GnPoolArgs a) {
-  constexpr int NT = kEpiThreads;
+// Lanes run along a row: each wavefront step ("unit") takes one row of
+// windows and a span of 64/k*k consecutive columns (whole windows), so
+// every load instruction reads consecutive floats and every element in a
+// window is loaded exactly once.  The k rows of a window are reduced
+// in-lane, then the k lanes of the window by shuffles (butterflies for
+// k = 4, KT = 4; any k with KT = 0).
+template <int KT>
+__global__ void __launch_bounds__(kEpiThreads) gn_plane_kernel(const GnPlaneArgs a) {
+  constexpr int NT = kEpiThreads, NWV = NT / 64;
   __shared__ double red0[NT / 64], red1[NT / 64];
-  const int64_t ng = blockIdx.x;  // n * groups + g
-  const int g = (int)(ng % a.groups);
-  const int tid = threadIdx.x;
-  const int64_t P = (int64_t)a.H * a.W;
-  const int64_t total = (int64_t)a.cpg * P;
-  const float* yb = a.y + ng * total;
+  const int64_t nc = blockIdx.x;  // n * C + c
+  const int c = (int)(nc % a.C);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the host keeps a plane below 2^31 floats: 32-bit indices)
+  const int P = a.H * a.W, PP = a.Ph * a.Pw;
+  const float* yb = a.y + nc * (int64_t)P;
+  float* ob = a.out + nc * (int64_t)PP;
+  const int k = KT ? KT : a.k;
+  const bool keep_max = (a.gamma[c] >= 0.0f) == (a.scale[c] >= 0.0f);
 
-  const double K = (double)yb[0];
-  double s1 = 0.0, s2 = 0.0;
-  if constexpr (VEC) {
-    const float4* y4 = reinterpret_cast<const float4*>(yb);
-    for (int64_t q = tid; q < total / 4; q += NT) {
-      const float4 v = y4[q];
-      const double d0 = (double)v.x - K, d1 = (double)v.y - K;
-      const double d2 = (double)v.z - K, d3 = (double)v.w - K;
-      s1 += (d0 + d1) + (d2 + d3);
-      s2 = fma(d0, d0, fma(d1, d1, fma(d2, d2, fma(d3, d3, s2))));
+  const float Kf = yb[0];
+  float s1 = 0.0f, s2 = 0.0f;
+  auto acc = [&](float v) {
+    const float d = v - Kf;
+    s1 += d;
+    s2 = fmaf(d, d, s2);
+  };
+  // pass 1a: the windows.  Each step issues the loads of UNR units before
+  // reducing any of them (one unit's loads alone would leave the
+  // wavefront waiting on one round trip to memory per unit).
+  const int span = (64 / k) * k;           // columns per unit
+  const int cw = a.Pw * k, rh = a.Ph * k;  // window-covered columns / rows
+  const int nsx = (cw + span - 1) / span;  // units per row of windows
+  const int nunits = a.Ph * nsx;
+  const int lead = lane - lane % k;        // first lane of this lane's window
+  constexpr int UNR = KT == 4 ? 4 : 1;
+  for (int u0 = wave; u0 < nunits; u0 += NWV * UNR) {
+    float v[UNR][KT == 4 ? 4 : 1];
+    int pyq[UNR], xq[UNR];
+    bool okq[UNR];
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) {
+      const int u = u0 + q * NWV;
+      const int py = u / nsx;
+      const int x = (u - py * nsx) * span + lane;
+      pyq[q] = py;
+      xq[q] = x;
+      okq[q] = u < nunits && lane < span && x < cw;
+      if constexpr (KT == 4) {
+        // (a unit past the end, or a lane past the windows, addresses the
+        // plane's first row instead, so no load can leave the plane)
+        const float* src = yb + (okq[q] ? py * 4 * a.W + x : 0);
+        // (unconditional loads from valid addresses: no branch separates
+        // them, so all UNR*4 are in flight together)
+#pragma unroll
+        for (int dy = 0; dy < 4; ++dy)
+          v[q][dy] = __builtin_nontemporal_load(src + dy * a.W);
+      }
     }
-  } else {
-    for (int64_t i = tid; i < total; i += NT) {
-      const double d = (double)yb[i] - K;
-      s1 += d;
-      s2 = fma(d, d, s2);
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) {
+      const bool ok = okq[q];
+      const int py = pyq[q], x = xq[q];
+      float mx = -__builtin_inff(), mn = __builtin_inff();
+      if constexpr (KT == 4) {
+        float wmx = fmaxf(fmaxf(v[q][0], v[q][1]), fmaxf(v[q][2], v[q][3]));
+        float wmn = fminf(fminf(v[q][0], v[q][1]), fminf(v[q][2], v[q][3]));
+#pragma unroll
+        for (int dy = 0; dy < 4; ++dy) {
+          const float d = ok ? v[q][dy] - Kf : 0.0f;
+          s1 += d;
+          s2 = fmaf(d, d, s2);
+        }
+        mx = ok ? wmx : mx;
+        mn = ok ? wmn : mn;
+        // the 4 lanes of a window are a quad
+        mx = fmaxf(mx, quad_swap<0xB1>(mx));
+        mn = fminf(mn, quad_swap<0xB1>(mn));
+        mx = fmaxf(mx, quad_swap<0x4E>(mx));
+        mn = fminf(mn, quad_swap<0x4E>(mn));
+      } else {
+        const float* src = yb + (ok ? py * k * a.W + x : 0);
+        for (int dy = 0; dy < k; ++dy) {
+          if (ok) {
+            const float w = __builtin_nontemporal_load(src + dy * a.W);
+            acc(w);
+            mx = fmaxf(mx, w);
+            mn = fminf(mn, w);
+          }
+        }
+        const float m0 = mx, n0 = mn;
+        for (int j = 1; j < k; ++j) {
+          mx = fmaxf(mx, __shfl(m0, lead + j, 64));
+          mn = fminf(mn, __shfl(n0, lead + j, 64));
+        }
+      }
+      if (ok && lane == lead) ob[py * a.Pw + x / k] = keep_max ? mx : mn;
     }
   }
-  const double S1 = block_sum_d<NT>(s1, red0);
-  const double S2 = block_sum_d<NT>(s2, red1);
-  const double N = (double)total;
-  const double m2 = fmax(S2 - S1 * S1 / N, 0.0);
-  const float mu = (float)(K + S1 / N);
-  const float rstd = (float)(1.0 / sqrt(m2 / N + (double)a.eps));
-
-  const int64_t PP = (int64_t)a.Ph * a.Pw;
-  float* ob = a.out + ng * a.cpg * PP;
-  const int c0 = g * a.cpg;
-  for (int64_t o = tid; o < a.cpg * PP; o += NT) {
-    const int c = (int)(o / PP);
-    const int64_t r = o - c * PP;
-    const int py = (int)(r / a.Pw), px = (int)(r - (int64_t)py * a.Pw);
-    const float A = rstd * a.gamma[c0 + c] * a.scale[c0 + c];
-    const float Bc = a.beta[c0 + c] * a.scale[c0 + c];
-    const float* src = yb + c * P + (int64_t)py * a.k * a.W + (int64_t)px * a.k;
-    float m = -__builtin_inff();
-    for (int dy = 0; dy < a.k; ++dy)
-      for (int dx = 0; dx < a.k; ++dx)
-        m = fmaxf(m, fmaf(src[(int64_t)dy * a.W + dx] - mu, A, Bc));
-    ob[o] = fminf(fmaxf(m, a.lo), a.hi);
+  // pass 1b: the remainder, the columns right of the last window (all
+  // rows), then the rows below the last window; 4 loads in flight
+  const int right = a.H * (a.W - cw), below = (a.H - rh) * cw;
+  const int rem = right + below;
+  for (int e0 = tid; e0 < rem; e0 += 4 * NT) {
+    float w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i0 = e0 + q * NT;
+      const int i = i0 < rem ? i0 : 0;  // (past the end: element 0 again)
+      int row, col;
+      if (i < right) {
+        row = i / (a.W - cw);
+        col = cw + (i - row * (a.W - cw));
+      } else {
+        const int j = i - right;
+        row = rh + j / cw;
+        col = j - (row - rh) * cw;
+      }
+      const float t = yb[row * a.W + col];
+      w[q] = i0 < rem ? t : Kf;  // (Kf adds nothing)
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc(w[q]);
+  }
+  const double S1 = block_sum_d<NT>((double)s1, red0);
+  const double S2 = block_sum_d<NT>((double)s2, red1);
+  if (tid == 0) {
+    const double n = (double)P;
+    a.part[nc] = make_float4((float)(n * (double)Kf + S1),
+                             (float)fmax(S2 - S1 * S1 / n, 0.0), (float)n, 0.0f);
   }
 }
 

@@ -206,9 +206,14 @@ X3_API x3_status x3_conv3x3_scale_min_f32(const float* x, const float* w,
 
 namespace {
 // Workspace of the GroupNorm entry point: the statistics partials of the
-// fused kernel (pool 4), or the whole conv output (other windows).
+// fused kernel (pool 4), or the whole conv output followed (at a 256-byte
+// boundary) by one partial per (sample, channel) plane (other windows).
+size_t split_y_bytes(const Shape& s) {
+  return ((size_t)s.B * s.Cout * s.Ho * s.Wo * sizeof(float) + 255) / 256 * 256;
+}
 size_t gn_workspace(const Shape& s, int groups, int pool_k) {
-  if (pool_k != 4) return (size_t)s.B * s.Cout * s.Ho * s.Wo * sizeof(float);
+  if (pool_k != 4)
+    return split_y_bytes(s) + (size_t)s.B * s.Cout * sizeof(float4);
   return (size_t)s.B * groups *
          x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups) *
          sizeof(float4);
@@ -245,6 +250,7 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
     return fail(X3_EUNSUPPORTED,
                 "one sample of out or of the workspace must be < 2 GiB");
   // other windows take the split path: the conv output is stored whole
+  // (and one group of it is indexed with 32 bits)
   if (pool_k != 4 && (uint64_t)x3i::padded_cout(Cout) * (H - 2) * (W - 2) * 4 >=
                          (1ull << 31))
     return fail(X3_EUNSUPPORTED, "one sample of the conv output must be < 2 GiB");
@@ -301,26 +307,22 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   hipStream_t st = (hipStream_t)stream;
   if (pool_k != 4) {
     // split path: conv output into the workspace, then the standalone
-    // GroupNorm -> scale -> pool -> clamp kernel
+    // GroupNorm -> scale -> pool -> clamp kernels
     rc = x3i::launch_conv_store(base_args(x, w, b, (float*)workspace, s), st);
     if (rc != X3_OK) return rc;
-    x3::GnPoolArgs g{};
+    x3::GnPlaneArgs g{};
     g.y = (const float*)workspace;
     g.gamma = gamma;
-    g.beta = beta;
     g.scale = scale;
     g.out = out;
-    g.groups = groups;
-    g.cpg = Cout / groups;
+    g.part = (float4*)((char*)workspace + split_y_bytes(s));
+    g.C = Cout;
     g.H = s.Ho;
     g.W = s.Wo;
     g.k = pool_k;
     g.Ph = Ph;
     g.Pw = Pw;
-    g.eps = eps;
-    g.lo = lo;
-    g.hi = hi;
-    return x3i::launch_epi_gn(g, (int64_t)B * groups, st);
+    return x3i::launch_epi_gn(g, B, groups, beta, eps, lo, hi, st);
   }
   x3::ConvArgs a = base_args(x, w, b, out, s);
   a.v0 = gamma;
@@ -441,10 +443,16 @@ X3_API x3_status x3_epi_mul_lrelu_gelu_tanh_f32(const float* y,
   return epi_gelu(y, mult, neg_slope, out, B, C, H, W, stream, true);
 }
 
+X3_API size_t x3_epi_gn_workspace_bytes(int B, int C) {
+  if (B < 0 || C < 1) return 0;
+  return (size_t)B * C * sizeof(float4);
+}
+
 X3_API x3_status x3_epi_gn_scale_pool_clamp_f32(
     const float* y, const float* gamma, const float* beta, const float* scale,
-    int groups, float eps, int pool_k, float lo, float hi, float* out, int B,
-    int C, int H, int W, void* stream) {
+    int groups, float eps, int pool_k, float lo, float hi, float* out,
+    void* workspace, size_t workspace_bytes, int B, int C, int H, int W,
+    void* stream) {
   x3_status rc = check_epi(y, out, B, C, H, W);
   if (rc != X3_OK) return rc;
   if (groups < 1) return fail(X3_EINVAL, "groups must be >= 1");
@@ -453,6 +461,8 @@ X3_API x3_status x3_epi_gn_scale_pool_clamp_f32(
     return fail(X3_ESHAPE, "C=%d is not divisible by groups=%d", C, groups);
   if (H < pool_k || W < pool_k)
     return fail(X3_ESHAPE, "input %dx%d is smaller than the pool window", H, W);
+  if ((uint64_t)H * W >= (1ull << 31))
+    return fail(X3_EUNSUPPORTED, "a plane of y must hold fewer than 2^31 floats");
   if (!gamma || !beta || !scale)
     return fail(X3_EINVAL, "null gamma/beta/scale pointer");
   if (!(eps > 0.0f) || !std::isfinite(eps))
@@ -460,29 +470,32 @@ X3_API x3_status x3_epi_gn_scale_pool_clamp_f32(
   if (!std::isfinite(lo) || !std::isfinite(hi) || lo > hi)
     return fail(X3_EINVAL, "clamp bounds must be finite with lo <= hi");
   if (B == 0) return X3_OK;
+  const size_t need = (size_t)B * C * sizeof(float4);
+  if (!workspace || workspace_bytes < need)
+    return fail(X3_EWORKSPACE, "workspace of %zu bytes needed, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 15u) != 0)
+    return fail(X3_EINVAL, "workspace must be 16-byte aligned");
   const int Ph = (H - pool_k) / pool_k + 1, Pw = (W - pool_k) / pool_k + 1;
   const size_t ob = (size_t)B * C * Ph * Pw * 4, cb = (size_t)C * 4;
-  if (overlaps(out, ob, y, (size_t)B * C * H * W * 4) ||
-      overlaps(out, ob, gamma, cb) || overlaps(out, ob, beta, cb) ||
-      overlaps(out, ob, scale, cb))
-    return fail(X3_EINVAL, "out overlaps an input");
-  x3::GnPoolArgs g{};
+  const size_t yb = (size_t)B * C * H * W * 4;
+  if (overlaps(out, ob, y, yb) || overlaps(out, ob, gamma, cb) ||
+      overlaps(out, ob, beta, cb) || overlaps(out, ob, scale, cb) ||
+      overlaps(out, ob, workspace, need) || overlaps(workspace, need, y, yb))
+    return fail(X3_EINVAL, "out or workspace overlaps another buffer");
+  x3::GnPlaneArgs g{};
   g.y = y;
   g.gamma = gamma;
-  g.beta = beta;
   g.scale = scale;
   g.out = out;
-  g.groups = groups;
-  g.cpg = C / groups;
+  g.part = (float4*)workspace;
+  g.C = C;
   g.H = H;
   g.W = W;
   g.k = pool_k;
   g.Ph = Ph;
   g.Pw = Pw;
-  g.eps = eps;
-  g.lo = lo;
-  g.hi = hi;
-  return x3i::launch_epi_gn(g, (int64_t)B * groups, (hipStream_t)stream);
+  return x3i::launch_epi_gn(g, B, groups, beta, eps, lo, hi, (hipStream_t)stream);
 }
 
 X3_API const char* x3_status_str(x3_status s) {
