@@ -281,10 +281,12 @@ __global__ void __launch_bounds__(kEpiThreads) gn_plane_kernel(const GnPlaneArgs
         // plane's first row instead, so no load can leave the plane)
         const float* src = yb + (okq[q] ? py * 4 * a.W + x : 0);
         // (unconditional loads from valid addresses: no branch separates
-        // them, so all UNR*4 are in flight together)
+        // them, so all UNR*4 are in flight together.  Ordinary, not
+        // streaming, loads: rows need not start on a cache line, and a line
+        // shared by two units or rows should survive until both used it.)
 #pragma unroll
         for (int dy = 0; dy < 4; ++dy)
-          v[q][dy] = __builtin_nontemporal_load(src + dy * a.W);
+          v[q][dy] = src[dy * a.W];
       }
     }
 #pragma unroll
@@ -312,7 +314,7 @@ __global__ void __launch_bounds__(kEpiThreads) gn_plane_kernel(const GnPlaneArgs
         const float* src = yb + (ok ? py * k * a.W + x : 0);
         for (int dy = 0; dy < k; ++dy) {
           if (ok) {
-            const float w = __builtin_nontemporal_load(src + dy * a.W);
+            const float w = src[dy * a.W];
             acc(w);
             mx = fmaxf(mx, w);
             mn = fminf(mn, w);
