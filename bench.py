@@ -247,6 +247,8 @@ def main():
                     help="do not time the other four workloads")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the unfused (conv + standalone epilogue) comparison")
+    ap.add_argument("--no-nhwc", action="store_true",
+                    help="skip timing the NHWC (channels_last) forms of the workloads")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -350,6 +352,38 @@ def main():
             abl[name] = ablation(torch, x3, WORKLOADS[name], dev, max(3, min(args.steps, 20)),
                                  max(1, min(args.warmup, 5)), fused[name])
 
+    # The NHWC (channels_last x) form of each workload, same values.
+    nhwc = {}
+    if not args.no_nhwc:
+        for name in WORKLOAD_ORDER:
+            w2 = WORKLOADS[name]
+            if w2.B * w2.Cout < 1024:
+                continue
+            log(f"nhwc {name}")
+            g2 = gpu_inputs(torch, w2, dev, seed=0)
+            g2["x"] = g2["x"].contiguous(memory_format=torch.channels_last)
+            o2 = None
+            if w2.op in ("mul_lrelu_gelu", "gn_scale_pool_clamp"):
+                o2 = torch.empty(out_shape(w2), device=dev, memory_format=torch.channels_last)
+            else:
+                o2 = torch.empty(out_shape(w2), device=dev)
+            ws2 = None
+            if w2.op == "gn_scale_pool_clamp":
+                q = w2.params
+                ws2 = torch.empty(x3.gn_workspace_bytes(w2.B, w2.Cin, w2.H, w2.W, w2.Cout,
+                                                        q["groups"], q["pool_k"], nhwc=True),
+                                  dtype=torch.uint8, device=dev)
+            op2 = make_op(x3, w2, g2, out=o2, workspace=ws2)
+            steps2 = max(3, min(args.steps, 20))
+            _, mk = time_op(torch, op2, steps2, max(1, min(args.warmup, 5)))
+            f2 = w2.conv_flops()
+            nhwc[name] = {"kernel_ms": round(mk, 4),
+                          "tflops": round(f2 / (mk * 1e-3) / 1e12, 3),
+                          "frac_fp32_mfma_peak": round(f2 / (mk * 1e-3) / 1e12 /
+                                                       PEAK_FP32_MFMA_TFLOPS, 4)}
+            del g2, o2, ws2, op2
+            torch.cuda.empty_cache()
+
     cpu = None
     parity = None
     if args.cpu_budget > 0:
@@ -379,6 +413,7 @@ def main():
         "parity": parity,
         "other_workloads": others,
         "unfused_ablation": abl,
+        "nhwc_workloads": nhwc,
         "host": {"cpu": platform.processor() or platform.machine(), "cpu_count": os.cpu_count(),
                  "device": torch.cuda.get_device_name(0)},
     }

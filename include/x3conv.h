@@ -193,6 +193,49 @@ x3_status x3_epi_gn_scale_pool_clamp_f32(const float* y, const float* gamma,
                                          size_t workspace_bytes, int B, int C,
                                          int H, int W, void* stream);
 
+/* ------------------------------------------------------------------------
+ * NHWC (channels-last) input: the same four fused operations with
+ *     x    [B][H][W][Cin]   (NHWC, contiguous)
+ * and the per-channel outputs channels-last too; w stays [Cout][Cin][3][3]
+ * and the per-channel vectors [Cout].  Two pages weigh this layout and keep
+ * NCHW: l2_p85 considers channels_last for its convolution, l2_p54 for
+ * coalesced staging of its direct convolution (channels contiguous per
+ * pixel).  It is the layout PyTorch's channels_last tensors hold.  Arguments,
+ * limits and errors are those of the NCHW entry points, except that the
+ * GroupNorm form supports pool_k == 4 only.
+ * ------------------------------------------------------------------------ */
+
+/* (a) on NHWC x; out [B][Ho][Wo] (the same bytes in either layout). */
+x3_status x3_conv3x3_min_tanh2_nhwc_f32(const float* x, const float* w,
+                                        const float* b, float* out, int B,
+                                        int Cin, int H, int W, int Cout,
+                                        void* stream);
+
+/* (b) on NHWC x; out [B][Ho][Wo][Cout]. */
+x3_status x3_conv3x3_mul_lrelu_gelu_nhwc_f32(const float* x, const float* w,
+                                             const float* b, const float* mult,
+                                             float neg_slope, float* out,
+                                             int B, int Cin, int H, int W,
+                                             int Cout, void* stream);
+
+/* (c) on NHWC x; out [B][Ho][Wo]. */
+x3_status x3_conv3x3_scale_min_nhwc_f32(const float* x, const float* w,
+                                        const float* b, float scale,
+                                        float* out, int B, int Cin, int H,
+                                        int W, int Cout, void* stream);
+
+/* Workspace bytes for x3_conv3x3_gn_scale_pool_clamp_nhwc_f32 (0 when the
+ * shape is invalid or unsupported). */
+size_t x3_conv3x3_gn_nhwc_workspace_bytes(int B, int Cin, int H, int W,
+                                          int Cout, int groups, int pool_k);
+
+/* (d) on NHWC x; out [B][Ph][Pw][Cout]; pool_k == 4. */
+x3_status x3_conv3x3_gn_scale_pool_clamp_nhwc_f32(
+    const float* x, const float* w, const float* b, const float* gamma,
+    const float* beta, const float* scale, int groups, float eps, int pool_k,
+    float lo, float hi, float* out, void* workspace, size_t workspace_bytes,
+    int B, int Cin, int H, int W, int Cout, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* x3_status_str(x3_status s);
 /* Detail of the last failing call on this thread ("" if none). */

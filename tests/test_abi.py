@@ -240,3 +240,31 @@ def test_standalone_epilogue_validation(lib):
     assert call(ws=fake(0x60000008)) == EINVAL   # misaligned workspace
     assert call(ws=O) == EINVAL                  # workspace overlaps out
     assert call(B=0, y=None, out=None) == OK
+
+
+def test_nhwc_entry_validation(lib):
+    s = P(0)
+    assert lib.x3_conv3x3_min_tanh2_nhwc_f32(X, W_, B_, O, -1, 16, 32, 32, 64, s) == EINVAL
+    assert lib.x3_conv3x3_min_tanh2_nhwc_f32(X, W_, B_, O, 2, 16, 32, 32, 1025, s) == EUNSUP
+    assert lib.x3_conv3x3_scale_min_nhwc_f32(X, W_, B_, float("nan"), O, 2, 16, 32, 32, 64,
+                                             s) == EINVAL
+    assert lib.x3_conv3x3_mul_lrelu_gelu_nhwc_f32(X, W_, B_, None, 0.01, O, 2, 16, 32, 32, 64,
+                                                  s) == EINVAL
+    assert lib.x3_conv3x3_min_tanh2_nhwc_f32(None, W_, B_, None, 0, 16, 32, 32, 64, s) == OK
+    # the NHWC GroupNorm form compiles only 4x4 windows
+    f = lib.x3_conv3x3_gn_nhwc_workspace_bytes
+    assert f(2, 8, 34, 34, 64, 16, 4) > 0
+    assert f(2, 8, 34, 34, 64, 16, 3) == 0
+    # [2,8,34,34] -> 32x32, Cin <= 8 and Cout <= 64: resident-weight tiles
+    # of 16 rows x 32 columns, 4 waves -> 2 * 1 * 4 = 8 slots
+    assert f(2, 8, 34, 34, 64, 16, 4) == 2 * 16 * 8 * 16
+    # Cin 16: 8-wave tiles of 32 rows x 32 columns -> 8 slots
+    assert f(2, 16, 34, 34, 64, 16, 4) == 2 * 16 * 8 * 16
+    # [*, 8, 128, 128] -> 126x126 resident: 16 row tiles x 2 column tiles x 4
+    assert f(1, 8, 128, 128, 64, 16, 4) == 16 * 16 * 2 * 4 * 16
+    g = lib.x3_conv3x3_gn_scale_pool_clamp_nhwc_f32
+    ws = fake(0x60000000)
+    assert g(X, W_, B_, M, fake(0x51000000), fake(0x52000000), 16, 1e-5, 3, 0.0, 1.0, O, ws,
+             1 << 20, 2, 8, 34, 34, 64, s) == EUNSUP
+    assert g(X, W_, B_, M, fake(0x51000000), fake(0x52000000), 16, 1e-5, 4, 0.0, 1.0, O, ws,
+             16, 2, 8, 34, 34, 64, s) == EWS

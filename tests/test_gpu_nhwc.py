@@ -1,0 +1,120 @@
+"""GPU parity of the NHWC (channels_last) input path against the oracle.
+
+The oracle works on NCHW arrays; the GPU call gets the same values in
+channels_last memory format and its outputs are compared by logical index.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import x3_conv2d_epilogue_amd as x3
+from x3_conv2d_epilogue_amd.synthetic import random_case
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-4
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_cl(d):
+    g = {k: v.to(DEV) for k, v in d.items()}
+    g["x"] = g["x"].contiguous(memory_format=torch.channels_last)
+    assert x3.is_nhwc(g["x"])
+    return g
+
+
+def close(got, ref, what, tol=TOL):
+    got = got.detach().cpu().numpy().astype(np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    say(f"  {what}: max_abs_err={err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= tol, f"{what}: {err:.3e}"
+
+
+# widths on each side of the tile-width switches (32, 64 output columns),
+# ragged rows and columns, Cin below / at / above / not a multiple of the
+# 8-channel K chunk
+SHAPES = [  # (B, Cin, H, W)
+    (2, 8, 21, 30),     # Wo=28: one 32-column strip
+    (1, 3, 35, 35),     # Wo=33: two strips, Cin=3
+    (2, 16, 13, 66),    # Wo=64
+    (1, 12, 20, 67),    # Wo=65: 128-column tiles, ragged
+    (1, 20, 9, 300),    # Wo=298: three column tiles, ragged
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("Cout", [40, 64, 128, 200])
+def test_nhwc_scale_min_integer_bit_exact(shape, Cout):
+    B, Cin, H, W = shape
+    say(f"nhwc scale_min int-exact {shape} Cout={Cout}")
+    d = random_case("scale_min", B, Cin, H, W, Cout, seed=1500 + Cout, dist="int")
+    g = dev_cl(d)
+    for s in (2.0, -1.0):
+        got = x3.conv3x3_scale_min(g["x"], g["weight"], g["bias"], s).cpu().numpy()
+        ref = oracle.scale_min(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(), s)
+        assert np.array_equal(got.astype(np.float64), ref), f"scale {s}"
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("Cout", [64, 128])
+def test_nhwc_min_tanh2(shape, Cout):
+    B, Cin, H, W = shape
+    say(f"nhwc min_tanh2 {shape} Cout={Cout}")
+    d = random_case("min_tanh2", B, Cin, H, W, Cout, seed=1600 + W)
+    g = dev_cl(d)
+    close(x3.conv3x3_min_tanh2(g["x"], g["weight"], g["bias"]),
+          oracle.min_tanh2(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy()), "min_tanh2")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("Cout", [17, 64, 128, 200])
+def test_nhwc_mul_lrelu_gelu(shape, Cout):
+    B, Cin, H, W = shape
+    say(f"nhwc gelu {shape} Cout={Cout}")
+    d = random_case("mul_lrelu_gelu", B, Cin, H, W, Cout, seed=1700 + Cout)
+    g = dev_cl(d)
+    out = x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"], 0.01)
+    assert Cout == 1 or out.is_contiguous(memory_format=torch.channels_last)
+    n = {k: v.numpy() for k, v in d.items()}
+    close(out, oracle.mul_lrelu_gelu(n["x"], n["weight"], n["bias"], n["multiplier"], 0.01),
+          "gelu")
+
+
+@pytest.mark.parametrize("shape", [(2, 8, 34, 34), (1, 3, 22, 39), (1, 16, 18, 131)])
+@pytest.mark.parametrize("cg", [(64, 16), (64, 8), (128, 32), (36, 9)])
+def test_nhwc_gn_pool(shape, cg):
+    Cout, groups = cg
+    B, Cin, H, W = shape
+    say(f"nhwc gn {shape} Cout={Cout} groups={groups}")
+    d = random_case("gn_scale_pool_clamp", B, Cin, H, W, Cout, seed=1800 + Cout + groups)
+    d["gamma"][::3] *= -1.0
+    g = dev_cl(d)
+    out = x3.conv3x3_gn_scale_pool_clamp(g["x"], g["weight"], g["bias"], g["gamma"], g["beta"],
+                                         g["scale"], groups, 1e-5, 4, -50.0, 50.0)
+    assert out.is_contiguous(memory_format=torch.channels_last)
+    n = {k: v.numpy() for k, v in d.items()}
+    close(out, oracle.gn_scale_pool_clamp(n["x"], n["weight"], n["bias"], n["gamma"], n["beta"],
+                                          n["scale"], groups, 1e-5, 4, -50.0, 50.0), "gn")
+
+
+def test_nhwc_matches_nchw_on_full_width_shape():
+    """One larger shape through both layouts: identical inputs, results
+    within the parity bar of each other (their summation orders match)."""
+    d = random_case("mul_lrelu_gelu", 2, 16, 40, 258, 64, seed=1900)
+    g = {k: v.to(DEV) for k, v in d.items()}
+    gc = dev_cl(d)
+    a = x3.conv3x3_min_tanh2(g["x"], g["weight"], g["bias"])
+    b = x3.conv3x3_min_tanh2(gc["x"], gc["weight"], gc["bias"])
+    assert torch.equal(a, b)
+    a = x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"])
+    b = x3.conv3x3_mul_lrelu_gelu(gc["x"], gc["weight"], gc["bias"], gc["multiplier"])
+    assert torch.equal(a, b.contiguous())

@@ -6,6 +6,9 @@ tensors, allocates outputs (and the GroupNorm workspace) with torch, and
 passes raw device pointers plus the current HIP stream to the C ABI.  Every
 step of the computation runs in the library's HIP kernels; there is no CPU or
 PyTorch fallback -- if the library is missing, every call raises.
+
+The fused ops follow x's memory format: a channels_last x selects the NHWC
+kernels, and per-channel outputs are then allocated channels_last too.
 """
 from __future__ import annotations
 
@@ -31,6 +34,9 @@ EXPORTED_SYMBOLS = (
     "x3_conv3x3_mul_lrelu_gelu_tanh_f32", "x3_conv3x3_bias_f32",
     "x3_conv3x3_scale_min_f32", "x3_conv3x3_gn_workspace_bytes",
     "x3_conv3x3_gn_scale_pool_clamp_f32",
+    "x3_conv3x3_min_tanh2_nhwc_f32", "x3_conv3x3_mul_lrelu_gelu_nhwc_f32",
+    "x3_conv3x3_scale_min_nhwc_f32", "x3_conv3x3_gn_nhwc_workspace_bytes",
+    "x3_conv3x3_gn_scale_pool_clamp_nhwc_f32",
     "x3_epi_min_tanh2_f32", "x3_epi_scale_min_f32", "x3_epi_mul_lrelu_gelu_f32",
     "x3_epi_mul_lrelu_gelu_tanh_f32", "x3_epi_gn_workspace_bytes",
     "x3_epi_gn_scale_pool_clamp_f32",
@@ -69,6 +75,14 @@ def load_library():
     lib.x3_conv3x3_mul_lrelu_gelu_f32.argtypes = [vp, vp, vp, vp, f, vp, i, i, i, i, i, vp]
     lib.x3_conv3x3_mul_lrelu_gelu_tanh_f32.argtypes = [vp, vp, vp, vp, f, vp, i, i, i, i, i, vp]
     lib.x3_conv3x3_bias_f32.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.x3_conv3x3_min_tanh2_nhwc_f32.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.x3_conv3x3_mul_lrelu_gelu_nhwc_f32.argtypes = [vp, vp, vp, vp, f, vp, i, i, i, i, i,
+                                                       vp]
+    lib.x3_conv3x3_scale_min_nhwc_f32.argtypes = [vp, vp, vp, f, vp, i, i, i, i, i, vp]
+    lib.x3_conv3x3_gn_nhwc_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.x3_conv3x3_gn_nhwc_workspace_bytes.restype = sz
+    lib.x3_conv3x3_gn_scale_pool_clamp_nhwc_f32.argtypes = [
+        vp, vp, vp, vp, vp, vp, i, f, i, f, f, vp, vp, sz, i, i, i, i, i, vp]
     lib.x3_epi_min_tanh2_f32.argtypes = [vp, vp, i, i, i, i, vp]
     lib.x3_epi_scale_min_f32.argtypes = [vp, f, vp, i, i, i, i, vp]
     lib.x3_epi_mul_lrelu_gelu_f32.argtypes = [vp, vp, f, vp, i, i, i, i, vp]
@@ -105,14 +119,17 @@ def _check(fn: str, status: int):
         raise X3Error(fn, status, detail)
 
 
-def _tensor(t: torch.Tensor, name: str, ndim: int) -> torch.Tensor:
+def _tensor(t: torch.Tensor, name: str, ndim: int, channels_last: bool = False) -> torch.Tensor:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device (cuda/hip) tensor")
-    if not t.is_contiguous():
+    if channels_last:
+        if not t.is_contiguous(memory_format=torch.channels_last):
+            raise ValueError(f"{name} must be contiguous in channels_last memory format")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
@@ -128,8 +145,15 @@ def _vec(t: torch.Tensor, name: str, n: int) -> torch.Tensor:
     return t
 
 
+def is_nhwc(x: torch.Tensor) -> bool:
+    """True for a 4-D tensor stored channels-last (and not also plain
+    contiguous, as tensors with one channel or a 1x1 plane are)."""
+    return (isinstance(x, torch.Tensor) and x.dim() == 4 and not x.is_contiguous()
+            and x.is_contiguous(memory_format=torch.channels_last))
+
+
 def _conv_inputs(x, w, b):
-    x = _tensor(x, "x", 4)
+    x = _tensor(x, "x", 4, channels_last=is_nhwc(x))
     w = _tensor(w, "weight", 4)
     B, Cin, H, W = x.shape
     Cout = w.shape[0]
@@ -142,10 +166,14 @@ def _conv_inputs(x, w, b):
     return x, w, b, B, Cin, H, W, Cout
 
 
-def _out(out, shape, like):
+def _out(out, shape, like, channels_last=False):
     if out is None:
+        if channels_last:
+            return torch.empty(shape, dtype=torch.float32, device=like.device,
+                               memory_format=torch.channels_last)
         return torch.empty(shape, dtype=torch.float32, device=like.device)
-    out = _tensor(out, "out", len(shape))
+    # (a channels-last output of one channel is also plain contiguous)
+    out = _tensor(out, "out", len(shape), channels_last=channels_last and shape[1] > 1)
     if tuple(out.shape) != tuple(shape):
         raise ValueError(f"out must be {tuple(shape)}, got {tuple(out.shape)}")
     if out.device != like.device:
@@ -166,7 +194,8 @@ def conv3x3_min_tanh2(x, weight, bias, out=None) -> torch.Tensor:
     lib = load_library()
     x, w, b, B, Cin, H, W, Cout = _conv_inputs(x, weight, bias)
     out = _out(out, (B, 1, max(H - 2, 0), max(W - 2, 0)), x)
-    _check("x3_conv3x3_min_tanh2_f32", lib.x3_conv3x3_min_tanh2_f32(
+    name = "x3_conv3x3_min_tanh2_nhwc_f32" if is_nhwc(x) else "x3_conv3x3_min_tanh2_f32"
+    _check(name, getattr(lib, name)(
         _ptr(x), _ptr(w), _ptr(b), _ptr(out), B, Cin, H, W, Cout, _stream(x.device)))
     return out
 
@@ -177,8 +206,10 @@ def conv3x3_mul_lrelu_gelu(x, weight, bias, multiplier, neg_slope=0.01,
     lib = load_library()
     x, w, b, B, Cin, H, W, Cout = _conv_inputs(x, weight, bias)
     m = _vec(multiplier, "multiplier", Cout)
-    out = _out(out, (B, Cout, max(H - 2, 0), max(W - 2, 0)), x)
-    _check("x3_conv3x3_mul_lrelu_gelu_f32", lib.x3_conv3x3_mul_lrelu_gelu_f32(
+    nhwc = is_nhwc(x)
+    out = _out(out, (B, Cout, max(H - 2, 0), max(W - 2, 0)), x, channels_last=nhwc)
+    name = "x3_conv3x3_mul_lrelu_gelu_nhwc_f32" if nhwc else "x3_conv3x3_mul_lrelu_gelu_f32"
+    _check(name, getattr(lib, name)(
         _ptr(x), _ptr(w), _ptr(b), _ptr(m), float(neg_slope), _ptr(out),
         B, Cin, H, W, Cout, _stream(x.device)))
     return out
@@ -212,15 +243,17 @@ def conv3x3_scale_min(x, weight, bias, scale=2.0, out=None) -> torch.Tensor:
     lib = load_library()
     x, w, b, B, Cin, H, W, Cout = _conv_inputs(x, weight, bias)
     out = _out(out, (B, 1, max(H - 2, 0), max(W - 2, 0)), x)
-    _check("x3_conv3x3_scale_min_f32", lib.x3_conv3x3_scale_min_f32(
+    name = "x3_conv3x3_scale_min_nhwc_f32" if is_nhwc(x) else "x3_conv3x3_scale_min_f32"
+    _check(name, getattr(lib, name)(
         _ptr(x), _ptr(w), _ptr(b), float(scale), _ptr(out), B, Cin, H, W, Cout,
         _stream(x.device)))
     return out
 
 
-def gn_workspace_bytes(B, Cin, H, W, Cout, groups=16, pool_k=4) -> int:
-    return int(load_library().x3_conv3x3_gn_workspace_bytes(B, Cin, H, W, Cout,
-                                                             groups, pool_k))
+def gn_workspace_bytes(B, Cin, H, W, Cout, groups=16, pool_k=4, nhwc=False) -> int:
+    lib = load_library()
+    fn = lib.x3_conv3x3_gn_nhwc_workspace_bytes if nhwc else lib.x3_conv3x3_gn_workspace_bytes
+    return int(fn(B, Cin, H, W, Cout, groups, pool_k))
 
 
 def conv3x3_gn_scale_pool_clamp(x, weight, bias, gamma, beta, scale, groups=16,
@@ -236,14 +269,17 @@ def conv3x3_gn_scale_pool_clamp(x, weight, bias, gamma, beta, scale, groups=16,
     k = int(pool_k)
     Ph = (Ho - k) // k + 1 if (k > 0 and Ho >= k) else 0
     Pw = (Wo - k) // k + 1 if (k > 0 and Wo >= k) else 0
-    out = _out(out, (B, Cout, Ph, Pw), x)
-    need = gn_workspace_bytes(B, Cin, H, W, Cout, groups, k)
+    nhwc = is_nhwc(x)
+    out = _out(out, (B, Cout, Ph, Pw), x, channels_last=nhwc)
+    need = gn_workspace_bytes(B, Cin, H, W, Cout, groups, k, nhwc)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     if workspace.device != x.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on x's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("x3_conv3x3_gn_scale_pool_clamp_f32", lib.x3_conv3x3_gn_scale_pool_clamp_f32(
+    name = ("x3_conv3x3_gn_scale_pool_clamp_nhwc_f32" if nhwc
+            else "x3_conv3x3_gn_scale_pool_clamp_f32")
+    _check(name, getattr(lib, name)(
         _ptr(x), _ptr(w), _ptr(b), _ptr(g), _ptr(be), _ptr(s), int(groups), float(eps), k,
         float(lo), float(hi), _ptr(out), _ptr(workspace), ws_bytes, B, Cin, H, W, Cout,
         _stream(x.device)))

@@ -95,14 +95,18 @@ struct ConvArgs {
   int ncb;          // channel-block passes per tile: ceil(Cout / COUT)
   int Ph, Pw;       // pooled output size (EPI_GN_POOL*)
   int groups;       // GroupNorm groups (EPI_GN_POOL*)
+  int flags;        // kOutVec4: NHWC out takes 16-byte stores (Cout % 4
+                    // == 0 and out 16-byte aligned)
 };
+
+constexpr int kOutVec4 = 1;
 
 // Largest Cout: per-channel constants of all channel blocks live in LDS.
 constexpr int kMaxCout = 1024;
 
 // Compile-time geometry of one kernel configuration.
 template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_, bool X4_,
-          bool RESW_ = false>
+          bool RESW_ = false, bool NHWC_ = false>
 struct Geo {
   static constexpr int MT = MT_;          // 32-channel MFMA blocks per pass
   static constexpr int CC = CC_;          // input channels per K chunk
@@ -115,6 +119,12 @@ struct Geo {
   // The weight tile stays resident in LDS for the whole kernel (only valid
   // when K fits one chunk, Cin <= CC); items then stage the input only.
   static constexpr bool RESW = RESW_;
+  // x (and the per-channel outputs) in NHWC order: the input tile is staged
+  // pixel-major, [XROWS][XCOLS][CCP], CCP = CC + 2.  With a pitch of 2 mod 4
+  // dwords per pixel, the 32 pixels x 2 adjacent channels of a B-fragment
+  // read (lane half h reads channel 2cp + h) fall in 64 distinct banks.
+  static constexpr bool NHWC = NHWC_;
+  static constexpr int CCP = CC + 2;
   static constexpr int NTHR = NWAVE * 64;
   static constexpr int COUT = 32 * MT;    // channels per pass
   static constexpr int TWC = 32 * NCT;    // output columns per tile
@@ -126,7 +136,8 @@ struct Geo {
   // banks.
   static constexpr int CS0 = XROWS * XP;
   static constexpr int CS = CS0 + ((32 - (CS0 % 64)) + 64) % 64;
-  static constexpr int XBUF = CC * CS;    // input dwords per stage
+  static constexpr int XBUF =             // input dwords per stage
+      NHWC ? (XROWS * XCOLS * CCP + 63) / 64 * 64 : CC * CS;
   static constexpr int KC = 9 * CC;       // K per chunk
   static constexpr int WP = KC + 1;       // odd weight-row pitch: conflict-free
   static constexpr int WBUF = COUT * WP;  // weight dwords per stage
@@ -149,7 +160,9 @@ struct Geo {
   static constexpr int NW = NTILE_N / NWAVE;  // N-tiles per wave
 
   static_assert(CC % 2 == 0, "CC must be even");
-  static_assert(XBUF % 256 == 0 && WBUF % 64 == 0, "whole staging blocks");
+  static_assert(!NHWC || (CC % 4 == 0 && !X4),
+                "NHWC: CC % 4 == 0 (pitch 2 mod 4), 4-byte staging");
+  static_assert(XBUF % XBLK == 0 && WBUF % 64 == 0, "whole staging blocks");
   static_assert(NTILE_N % NWAVE == 0, "N-tiles must split evenly over waves");
   static_assert(TH % NW == 0, "a wave's N-tiles must lie in one strip");
   static_assert(LDS_DWORDS * 4 + 2 * kMaxCout * 4 <= 160 * 1024,
@@ -317,7 +330,7 @@ __global__ void __launch_bounds__(G::NTHR)
   struct Lim {
     __amdgpu_buffer_rsrc_t xr;
     int base;      // element offset of (ci0, r0, c0) in the sample
-    int ci_lim;    // local channels < ci_lim are real
+    int ci_lim;    // local channels < ci_lim are real (NHWC: and < CC)
     int row_lim;   // local rows < row_lim are real
     int col_lim;   // local columns < col_lim are needed and real
     int kk_lim;    // weight columns < kk_lim are real
@@ -327,8 +340,14 @@ __global__ void __launch_bounds__(G::NTHR)
   auto lim_of = [&](const Item& it) X3_INLINE {
     Lim l;
     l.xr = make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
-    l.base = (it.ci0 * a.H + it.r0) * a.W + it.c0;
-    l.ci_lim = a.Cin - it.ci0;
+    if constexpr (G::NHWC) {
+      l.base = (it.r0 * a.W + it.c0) * a.Cin + it.ci0;
+      const int cl = a.Cin - it.ci0;
+      l.ci_lim = cl < G::CC ? cl : G::CC;
+    } else {
+      l.base = (it.ci0 * a.H + it.r0) * a.W + it.c0;
+      l.ci_lim = a.Cin - it.ci0;
+    }
     const int rl = a.H - it.r0;
     l.row_lim = rl < G::XROWS ? rl : G::XROWS;
     const int cl = a.W - it.c0;
@@ -348,7 +367,26 @@ __global__ void __launch_bounds__(G::NTHR)
     // every buffer here is smaller than 2 GiB, so such an offset is past
     // num_records and the load returns 0.  (An OR rather than a select
     // keeps the compiler from turning this into an exec-masked region.)
-    if (i < G::NBI) {
+    if (i < G::NBI && G::NHWC) {
+      int blk = wave + zz + i * G::NWAVE;
+      blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
+      // LDS dword p of the tile is (pixel p / CCP, channel slot p % CCP);
+      // slots >= CC are padding, read as zero.  Consecutive lanes walk the
+      // channels of one pixel, then the next pixel of the row.
+      const uint32_t p = (uint32_t)(blk * 64 + lane);
+      const uint32_t pix = p / G::CCP;
+      const uint32_t slot = p - pix * G::CCP;
+      const uint32_t row = pix / G::XCOLS;
+      const uint32_t col = pix - row * G::XCOLS;
+      const bool ok = (slot < (uint32_t)l.ci_lim) &
+                      (row < (uint32_t)l.row_lim) &
+                      (col < (uint32_t)l.col_lim);
+      const uint32_t off =
+          (((row * (uint32_t)a.W + col) * (uint32_t)a.Cin + slot +
+            (uint32_t)l.base) << 2) | ((uint32_t)!ok << 31);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          l.xr, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
+    } else if (i < G::NBI) {
       int blk = wave + zz + i * G::NWAVE;
       blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
       // first dword of this lane's piece; with X4 the lane moves 4
@@ -489,7 +527,9 @@ __global__ void __launch_bounds__(G::NTHR)
       const float slope = a.s0;
       // bounded stores into this sample's [Cout][Ho][Wo] block; an offset
       // with bit 31 set (pixel outside the output) is dropped
-      // (padded channels land past the end of the block and are dropped)
+      // (NCHW: padded channels land past the end of the block and are
+      // dropped; NHWC: they would land in the next pixel, so they get the
+      // drop bit)
       const int HoWo = a.Ho * a.Wo;
       const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
           a.out + (size_t)n * a.Cout * HoWo, (uint32_t)(a.Cout * HoWo * 4));
@@ -497,8 +537,41 @@ __global__ void __launch_bounds__(G::NTHR)
 #pragma unroll
       for (int j = 0; j < G::NW; ++j) {
         const int r = r_base + j;
-        pix_off[j] = (uint32_t)(r * a.Wo + c);
+        pix_off[j] = (uint32_t)(r * a.Wo + c) * (G::NHWC ? (uint32_t)a.Cout : 1u);
         drop[j] = (uint32_t)!(col_ok && r < a.Ho) << 31;
+      }
+      auto op = [&](float y, float mv) X3_INLINE {
+        if constexpr (EPI != EPI_STORE) {
+          const float v = lrelu(y * mv, slope);
+          y = (EPI == EPI_MUL_LRELU_GELU) ? gelu_erf(v) : gelu_tanh(v);
+        }
+        return y;
+      };
+      if (G::NHWC && (a.flags & kOutVec4)) {
+        // NHWC with 16-byte stores: accumulator elements 4q..4q+3 are 4
+        // consecutive channels of one pixel (a multiple of 4, so with
+        // Cout % 4 == 0 the 4 are real or padded together)
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int co = co0 + mt * 32 + 8 * q + 4 * h;
+            const uint32_t pad = (uint32_t)(co >= a.Cout) << 31;
+            float mv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mv[e] = s_par[co + e];
+#pragma unroll
+            for (int j = 0; j < G::NW; ++j) {
+              u32x4 v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                v[e] = __builtin_bit_cast(uint32_t, op(acc[mt][j][4 * q + e], mv[e]));
+              const uint32_t off =
+                  ((pix_off[j] + (uint32_t)co) << 2) | drop[j] | pad;
+              __builtin_amdgcn_raw_buffer_store_b128(v, o_rsrc, off, 0, 0);
+            }
+          }
+        return;
       }
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
@@ -506,16 +579,15 @@ __global__ void __launch_bounds__(G::NTHR)
         for (int i = 0; i < 16; ++i) {
           const int co = co0 + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
           const float mv = s_par[co];
+          const uint32_t co_off =
+              G::NHWC ? (uint32_t)co | ((uint32_t)(co >= a.Cout) << 31)
+                      : (uint32_t)co * HoWo;
 #pragma unroll
           for (int j = 0; j < G::NW; ++j) {
-            float y = acc[mt][j][i];
-            if constexpr (EPI != EPI_STORE) {
-              const float v = lrelu(y * mv, slope);
-              y = (EPI == EPI_MUL_LRELU_GELU) ? gelu_erf(v) : gelu_tanh(v);
-            }
+            const float y = op(acc[mt][j][i], mv);
             // (OR, not add: nothing can clear the drop bit)
-            const uint32_t off =
-                (((uint32_t)co * HoWo + pix_off[j]) << 2) | drop[j];
+            const uint32_t off = ((co_off + pix_off[j]) << 2) | drop[j] |
+                                 (co_off & 0x80000000u);
             __builtin_amdgcn_raw_buffer_store_b32(
                 __builtin_bit_cast(uint32_t, y), o_rsrc, off, 0, 0);
           }
@@ -697,7 +769,12 @@ __global__ void __launch_bounds__(G::NTHR)
           const float vmn = e == 0 ? mn[0] : (e == 1 ? mn[1] : (e == 2 ? mn[2] : mn[3]));
           const int co = co0 + mt * 32 + 8 * q + 4 * h + e;
           const float v = (s_par[co] != 0.0f) ? vmx : vmn;
-          const uint32_t off = (((uint32_t)co * PP + win_off) << 2) | win_bad;
+          // NCHW: channel planes (padded channels fall past the end);
+          // NHWC: channels innermost (padded channels get the drop bit)
+          const uint32_t off =
+              G::NHWC ? ((win_off * (uint32_t)a.Cout + (uint32_t)co) << 2) |
+                            win_bad | ((uint32_t)(co >= a.Cout) << 31)
+                      : (((uint32_t)co * PP + win_off) << 2) | win_bad;
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v),
                                                 o_rsrc, off, 0, 0);
         }
@@ -742,7 +819,8 @@ __global__ void __launch_bounds__(G::NTHR)
     }
 
     const X3_LDS float* xs =
-        cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
+        G::NHWC ? cur + (wm.row0 * G::XCOLS + wm.strip * 32 + l32) * G::CCP + h
+                : cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
     const X3_LDS float* ws =
         (G::RESW ? (const X3_LDS float*)ldsw : cur + G::XBUF) + l32 * G::WP +
         h * 9;
@@ -760,7 +838,8 @@ __global__ void __launch_bounds__(G::NTHR)
         A[mt] = ws[mt * 32 * G::WP + cp * 18 + tap];
 #pragma unroll
       for (int j = 0; j < G::NW; ++j)
-        Bv[j] = xs[2 * cp * G::CS + (j + kh) * G::XP + kw];
+        Bv[j] = G::NHWC ? xs[((j + kh) * G::XCOLS + kw) * G::CCP + 2 * cp]
+                        : xs[2 * cp * G::CS + (j + kh) * G::XP + kw];
     };
     load_frag(0, av[0], bv[0]);
 #pragma unroll
@@ -837,6 +916,8 @@ struct GnFinArgs {
   const float* scale;
   float* out;
   int groups, cpg;   // groups, channels per group
+  int C;             // channels (NHWC finalize: the channel stride of out)
+  int nchunk;        // NHWC finalize: workgroups per sample
   int pps;           // partials per (sample, group)
   int plane;         // Ph * Pw
   float eps, lo, hi;
@@ -867,6 +948,34 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 // Wo), mean = sum_k sum_k / N and M2 = sum_k [M2_k + n_k (sum_k/n_k -
 // mean)^2] (the parallel-variance combination of Chan, Golub and LeVeque),
 // accumulated in double.
+// Group statistics from the partials p[0..pps) (p0 = p[threadIdx.x], or
+// zeros past pps, already loaded by the caller): mean and 1/sqrt(var+eps).
+template <int NT>
+__device__ __forceinline__ void gn_group_stats(const GnFinArgs& a,
+                                               const float4* p, float4 p0,
+                                               double* red0, double* red1,
+                                               float& mu, float& rstd) {
+  const int tid = threadIdx.x;
+  double sum = (double)p0.x;
+  for (int k = tid + NT; k < a.pps; k += NT) sum += (double)p[k].x;
+  const double mean = block_sum<NT>(sum, red0) / a.count;
+  double m2 = 0.0;
+  if (p0.z > 0.0f) {
+    const double d = (double)p0.x / (double)p0.z - mean;
+    m2 = (double)p0.y + (double)p0.z * d * d;
+  }
+  for (int k = tid + NT; k < a.pps; k += NT) {
+    const float4 v = p[k];
+    if (v.z > 0.0f) {
+      const double d = (double)v.x / (double)v.z - mean;
+      m2 += (double)v.y + (double)v.z * d * d;
+    }
+  }
+  m2 = block_sum<NT>(m2, red1);
+  mu = (float)mean;
+  rstd = (float)(1.0 / sqrt(m2 / a.count + (double)a.eps));
+}
+
 template <int NT, bool VEC>
 __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
   static_assert(NT % 64 == 0 && NT <= 1024, "whole wavefronts");
@@ -889,24 +998,8 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
     else
       first.x = o[tid];
   }
-  double sum = (double)p0.x;
-  for (int k = tid + NT; k < a.pps; k += NT) sum += (double)p[k].x;
-  const double mean = block_sum<NT>(sum, red0) / a.count;
-  double m2 = 0.0;
-  if (p0.z > 0.0f) {
-    const double d = (double)p0.x / (double)p0.z - mean;
-    m2 = (double)p0.y + (double)p0.z * d * d;
-  }
-  for (int k = tid + NT; k < a.pps; k += NT) {
-    const float4 v = p[k];
-    if (v.z > 0.0f) {
-      const double d = (double)v.x / (double)v.z - mean;
-      m2 += (double)v.y + (double)v.z * d * d;
-    }
-  }
-  m2 = block_sum<NT>(m2, red1);
-  const float mu = (float)mean;
-  const float rstd = (float)(1.0 / sqrt(m2 / a.count + (double)a.eps));
+  float mu, rstd;
+  gn_group_stats<NT>(a, p, p0, red0, red1, mu, rstd);
 
   // z = ((v - mu) * rstd * gamma + beta) * scale = (v - mu) * A + Bc, with
   // A = rstd*gamma*scale and Bc = beta*scale per channel; monotone in v
@@ -961,6 +1054,73 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
     }
   }
 #undef X3_GN_OUT
+}
+
+// The finalize for pooled extrema stored NHWC, out [B][Ph][Pw][C]: the
+// channels of one pooled position are contiguous, so a workgroup takes a
+// contiguous chunk of one sample's [plane][C] block (all groups) and moves
+// it with 16-byte accesses (VEC: C % 4 == 0, out 16-byte aligned).  It
+// first merges the statistics of every group of the sample (one wavefront
+// per group at a time; the partials are few and L2-resident) into
+// per-channel constants in LDS.
+template <int NT>
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int mask = 1; mask < 64; mask <<= 1) v += __shfl_xor(v, mask, 64);
+  return v;
+}
+
+constexpr int kFinNhwcPerThread = 8;  // float4 (or floats) per thread
+
+template <int NT, bool VEC>
+__global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a) {
+  __shared__ float s_mu[kMaxCout], s_A[kMaxCout], s_B[kMaxCout];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = blockIdx.x / a.nchunk, chunk = blockIdx.x - n * a.nchunk;
+  for (int g = wave; g < a.groups; g += NT / 64) {
+    const float4* p = a.part + ((size_t)n * a.groups + g) * a.pps;
+    double sum = 0.0;
+    for (int k = lane; k < a.pps; k += 64) sum += (double)p[k].x;
+    const double mean = wave_sum_d<NT>(sum) / a.count;
+    double m2 = 0.0;
+    for (int k = lane; k < a.pps; k += 64) {
+      const float4 v = p[k];
+      if (v.z > 0.0f) {
+        const double d = (double)v.x / (double)v.z - mean;
+        m2 += (double)v.y + (double)v.z * d * d;
+      }
+    }
+    m2 = wave_sum_d<NT>(m2);
+    const float rstd = (float)(1.0 / sqrt(m2 / a.count + (double)a.eps));
+    for (int c = g * a.cpg + lane; c < (g + 1) * a.cpg; c += 64) {
+      s_mu[c] = (float)mean;
+      s_A[c] = rstd * a.gamma[c] * a.scale[c];
+      s_B[c] = a.beta[c] * a.scale[c];
+    }
+  }
+  __syncthreads();
+  float* o = a.out + (size_t)n * a.plane * a.C;
+  const int total = a.plane * a.C;
+  const int span = NT * kFinNhwcPerThread;
+  if constexpr (VEC) {
+    float4* o4 = reinterpret_cast<float4*>(o);
+    const int end = min((chunk + 1) * span, total / 4);
+    for (int k = chunk * span + tid; k < end; k += NT) {
+      const int c = (4 * k) % a.C;  // 4 consecutive channels (C % 4 == 0)
+      float4 v = o4[k];
+      v.x = fminf(fmaxf(fmaf(v.x - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
+      v.y = fminf(fmaxf(fmaf(v.y - s_mu[c + 1], s_A[c + 1], s_B[c + 1]), a.lo), a.hi);
+      v.z = fminf(fmaxf(fmaf(v.z - s_mu[c + 2], s_A[c + 2], s_B[c + 2]), a.lo), a.hi);
+      v.w = fminf(fmaxf(fmaf(v.w - s_mu[c + 3], s_A[c + 3], s_B[c + 3]), a.lo), a.hi);
+      o4[k] = v;
+    }
+  } else {
+    const int end = min((chunk + 1) * span, total);
+    for (int k = chunk * span + tid; k < end; k += NT) {
+      const int c = k % a.C;
+      o[k] = fminf(fmaxf(fmaf(o[k] - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
+    }
+  }
 }
 
 }  // namespace x3

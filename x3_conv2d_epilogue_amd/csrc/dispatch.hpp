@@ -121,6 +121,13 @@ x3_status launch_epi_gn(const x3::GnPlaneArgs& g, int64_t B, int groups,
 x3_status launch_gn_pool(const x3::ConvArgs& a, hipStream_t st);
 x3_status launch_gn_finalize(const x3::GnFinArgs& f, int nblocks,
                              hipStream_t st);
+// NHWC x: the fused conv with epilogue `epi` (EPI_MIN_TANH2,
+// EPI_MUL_LRELU_GELU, EPI_SCALE_MIN, EPI_GN_POOL, EPI_GN_POOL_CH), the NHWC
+// GroupNorm finalize, and the GroupNorm partial slots of the NHWC tiles.
+x3_status launch_nhwc(const x3::ConvArgs& a, int epi, hipStream_t st);
+x3_status launch_gn_finalize_nhwc(x3::GnFinArgs f, int B, hipStream_t st);
+int gn_pps_nhwc(int Ho, int Wo, int Cin, int Cout);
+
 // GroupNorm partial slots per (sample, group or channel) for this shape: one
 // per wavefront tile of the configuration launch_gn_pool picks.
 int gn_pps(int Ho, int Wo, int Cin, int Cout);

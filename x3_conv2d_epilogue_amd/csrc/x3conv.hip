@@ -116,19 +116,44 @@ x3::ConvArgs base_args(const float* x, const float* w, const float* b,
 // ============================================================================
 // C ABI
 
-X3_API x3_status x3_conv3x3_min_tanh2_f32(const float* x, const float* w,
-                                          const float* b, float* out, int B,
-                                          int Cin, int H, int W, int Cout,
-                                          void* stream) {
+namespace {
+// The two channel-min entry points, either layout of x (out [B][Ho][Wo] is
+// the same in both).
+x3_status conv_channel_min(const float* x, const float* w, const float* b,
+                           float scale, float* out, int B, int Cin, int H,
+                           int W, int Cout, void* stream, int epi, bool nhwc) {
   Shape s;
   x3_status rc = check_common(x, w, b, out, B, Cin, H, W, Cout, s);
   if (rc != X3_OK) return rc;
+  if (!std::isfinite(scale)) return fail(X3_EINVAL, "scale must be finite");
   if (B == 0) return X3_OK;
   const size_t ob = (size_t)B * s.Ho * s.Wo * 4;
   if (overlaps(out, ob, x, s.x_bytes()) || overlaps(out, ob, w, s.w_bytes()) ||
       overlaps(out, ob, b, s.c_bytes()))
     return fail(X3_EINVAL, "out overlaps an input");
-  return x3i::launch_min_tanh2(base_args(x, w, b, out, s), (hipStream_t)stream);
+  x3::ConvArgs a = base_args(x, w, b, out, s);
+  a.s0 = scale;
+  const hipStream_t st = (hipStream_t)stream;
+  if (nhwc) return x3i::launch_nhwc(a, epi, st);
+  return epi == x3::EPI_MIN_TANH2 ? x3i::launch_min_tanh2(a, st)
+                                  : x3i::launch_scale_min(a, st);
+}
+}  // namespace
+
+X3_API x3_status x3_conv3x3_min_tanh2_f32(const float* x, const float* w,
+                                          const float* b, float* out, int B,
+                                          int Cin, int H, int W, int Cout,
+                                          void* stream) {
+  return conv_channel_min(x, w, b, 1.0f, out, B, Cin, H, W, Cout, stream,
+                          x3::EPI_MIN_TANH2, false);
+}
+
+X3_API x3_status x3_conv3x3_min_tanh2_nhwc_f32(const float* x, const float* w,
+                                               const float* b, float* out,
+                                               int B, int Cin, int H, int W,
+                                               int Cout, void* stream) {
+  return conv_channel_min(x, w, b, 1.0f, out, B, Cin, H, W, Cout, stream,
+                          x3::EPI_MIN_TANH2, true);
 }
 
 namespace {
@@ -137,7 +162,7 @@ namespace {
 x3_status conv_elementwise(const float* x, const float* w, const float* b,
                            const float* mult, float neg_slope, float* out,
                            int B, int Cin, int H, int W, int Cout, void* stream,
-                           bool store_only, bool tanh_form) {
+                           bool store_only, bool tanh_form, bool nhwc) {
   Shape s;
   x3_status rc = check_common(x, w, b, out, B, Cin, H, W, Cout, s);
   if (rc != X3_OK) return rc;
@@ -155,6 +180,10 @@ x3_status conv_elementwise(const float* x, const float* w, const float* b,
   x3::ConvArgs a = base_args(x, w, b, out, s);
   a.v0 = mult;
   a.s0 = neg_slope;
+  if (nhwc) {
+    if (Cout % 4 == 0 && ((uintptr_t)out & 15u) == 0) a.flags |= x3::kOutVec4;
+    return x3i::launch_nhwc(a, x3::EPI_MUL_LRELU_GELU, (hipStream_t)stream);
+  }
   if (store_only) return x3i::launch_conv_store(a, (hipStream_t)stream);
   return tanh_form ? x3i::launch_mul_lrelu_gelu_tanh(a, (hipStream_t)stream)
                    : x3i::launch_mul_lrelu_gelu(a, (hipStream_t)stream);
@@ -165,7 +194,7 @@ X3_API x3_status x3_conv3x3_bias_f32(const float* x, const float* w,
                                      const float* b, float* y, int B, int Cin,
                                      int H, int W, int Cout, void* stream) {
   return conv_elementwise(x, w, b, nullptr, 0.0f, y, B, Cin, H, W, Cout,
-                          stream, true, false);
+                          stream, true, false, false);
 }
 
 X3_API x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
@@ -175,7 +204,15 @@ X3_API x3_status x3_conv3x3_mul_lrelu_gelu_f32(const float* x, const float* w,
                                                int B, int Cin, int H, int W,
                                                int Cout, void* stream) {
   return conv_elementwise(x, w, b, mult, neg_slope, out, B, Cin, H, W, Cout,
-                          stream, false, false);
+                          stream, false, false, false);
+}
+
+X3_API x3_status x3_conv3x3_mul_lrelu_gelu_nhwc_f32(
+    const float* x, const float* w, const float* b, const float* mult,
+    float neg_slope, float* out, int B, int Cin, int H, int W, int Cout,
+    void* stream) {
+  return conv_elementwise(x, w, b, mult, neg_slope, out, B, Cin, H, W, Cout,
+                          stream, false, false, true);
 }
 
 X3_API x3_status x3_conv3x3_mul_lrelu_gelu_tanh_f32(
@@ -183,25 +220,24 @@ X3_API x3_status x3_conv3x3_mul_lrelu_gelu_tanh_f32(
     float neg_slope, float* out, int B, int Cin, int H, int W, int Cout,
     void* stream) {
   return conv_elementwise(x, w, b, mult, neg_slope, out, B, Cin, H, W, Cout,
-                          stream, false, true);
+                          stream, false, true, false);
 }
 
 X3_API x3_status x3_conv3x3_scale_min_f32(const float* x, const float* w,
                                           const float* b, float scale,
                                           float* out, int B, int Cin, int H,
                                           int W, int Cout, void* stream) {
-  Shape s;
-  x3_status rc = check_common(x, w, b, out, B, Cin, H, W, Cout, s);
-  if (rc != X3_OK) return rc;
-  if (!std::isfinite(scale)) return fail(X3_EINVAL, "scale must be finite");
-  if (B == 0) return X3_OK;
-  const size_t ob = (size_t)B * s.Ho * s.Wo * 4;
-  if (overlaps(out, ob, x, s.x_bytes()) || overlaps(out, ob, w, s.w_bytes()) ||
-      overlaps(out, ob, b, s.c_bytes()))
-    return fail(X3_EINVAL, "out overlaps an input");
-  x3::ConvArgs a = base_args(x, w, b, out, s);
-  a.s0 = scale;
-  return x3i::launch_scale_min(a, (hipStream_t)stream);
+  return conv_channel_min(x, w, b, scale, out, B, Cin, H, W, Cout, stream,
+                          x3::EPI_SCALE_MIN, false);
+}
+
+X3_API x3_status x3_conv3x3_scale_min_nhwc_f32(const float* x, const float* w,
+                                               const float* b, float scale,
+                                               float* out, int B, int Cin,
+                                               int H, int W, int Cout,
+                                               void* stream) {
+  return conv_channel_min(x, w, b, scale, out, B, Cin, H, W, Cout, stream,
+                          x3::EPI_SCALE_MIN, true);
 }
 
 namespace {
@@ -211,16 +247,22 @@ namespace {
 size_t split_y_bytes(const Shape& s) {
   return ((size_t)s.B * s.Cout * s.Ho * s.Wo * sizeof(float) + 255) / 256 * 256;
 }
-size_t gn_workspace(const Shape& s, int groups, int pool_k) {
+// Partials the finalize merges per (sample, group): one per wavefront tile,
+// times the group's channels where the partials are per channel.
+int gn_parts(const Shape& s, int groups, bool nhwc) {
+  if (!nhwc) return x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups);
+  const int slots = x3i::gn_pps_nhwc(s.Ho, s.Wo, s.Cin, s.Cout);
+  return x3i::gn_partials_per_channel(s.Cout, groups) ? slots * (s.Cout / groups)
+                                                      : slots;
+}
+size_t gn_workspace(const Shape& s, int groups, int pool_k, bool nhwc) {
   if (pool_k != 4)
     return split_y_bytes(s) + (size_t)s.B * s.Cout * sizeof(float4);
-  return (size_t)s.B * groups *
-         x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups) *
-         sizeof(float4);
+  return (size_t)s.B * groups * gn_parts(s, groups, nhwc) * sizeof(float4);
 }
 
 x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
-                   int pool_k, Shape& s) {
+                   int pool_k, bool nhwc, Shape& s) {
   if (B < 0 || Cin < 1 || H < 1 || W < 1 || Cout < 1)
     return fail(X3_EINVAL, "sizes must be positive (B >= 0)");
   if (groups < 1) return fail(X3_EINVAL, "groups must be >= 1");
@@ -234,6 +276,8 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
                 H - 2, W - 2);
   if (Cout > x3::kMaxCout)
     return fail(X3_EUNSUPPORTED, "Cout=%d exceeds %d", Cout, x3::kMaxCout);
+  if (nhwc && pool_k != 4)
+    return fail(X3_EUNSUPPORTED, "NHWC: pool_k=%d not compiled in (4)", pool_k);
   if ((uint64_t)Cin * H * W * 4 >= (1ull << 31))
     return fail(X3_EUNSUPPORTED, "one sample of x must be smaller than 2 GiB");
   // (the kernel works in 64-channel blocks: padded channels and groups
@@ -244,9 +288,10 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
   const uint64_t cpad = (uint64_t)(Cout + 63) / 64 * 64;
   const uint64_t prows =
       x3i::gn_partials_per_channel(Cout, groups) ? cpad : cpad / 4;
+  const uint64_t slots = nhwc ? x3i::gn_pps_nhwc(H - 2, W - 2, Cin, Cout)
+                              : x3i::gn_pps(H - 2, W - 2, Cin, Cout);
   if (pool_k == 4 &&
-      (cpad * P * 4 >= (1ull << 31) ||
-       prows * x3i::gn_pps(H - 2, W - 2, Cin, Cout) * 16 >= (1ull << 31)))
+      (cpad * P * 4 >= (1ull << 31) || prows * slots * 16 >= (1ull << 31)))
     return fail(X3_EUNSUPPORTED,
                 "one sample of out or of the workspace must be < 2 GiB");
   // other windows take the split path: the conv output is stored whole
@@ -259,25 +304,26 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
 }
 }  // namespace
 
-X3_API size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W,
-                                            int Cout, int groups, int pool_k) {
+namespace {
+size_t gn_workspace_query(int B, int Cin, int H, int W, int Cout, int groups,
+                          int pool_k, bool nhwc) {
   Shape s;
   char saved[sizeof(g_err)];
   __builtin_memcpy(saved, g_err, sizeof(g_err));
-  const x3_status rc = check_gn(B, Cin, H, W, Cout, groups, pool_k, s);
+  const x3_status rc = check_gn(B, Cin, H, W, Cout, groups, pool_k, nhwc, s);
   __builtin_memcpy(g_err, saved, sizeof(g_err));
   if (rc != X3_OK) return 0;
-  return gn_workspace(s, groups, pool_k);
+  return gn_workspace(s, groups, pool_k, nhwc);
 }
 
-X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
-    const float* x, const float* w, const float* b, const float* gamma,
-    const float* beta, const float* scale, int groups, float eps, int pool_k,
-    float lo, float hi, float* out, void* workspace, size_t workspace_bytes,
-    int B, int Cin, int H, int W, int Cout, void* stream) {
+x3_status gn_entry(const float* x, const float* w, const float* b,
+                   const float* gamma, const float* beta, const float* scale,
+                   int groups, float eps, int pool_k, float lo, float hi,
+                   float* out, void* workspace, size_t workspace_bytes, int B,
+                   int Cin, int H, int W, int Cout, void* stream, bool nhwc) {
   g_err[0] = '\0';
   Shape s;
-  x3_status rc = check_gn(B, Cin, H, W, Cout, groups, pool_k, s);
+  x3_status rc = check_gn(B, Cin, H, W, Cout, groups, pool_k, nhwc, s);
   if (rc != X3_OK) return rc;
   if (!w || !b || !gamma || !beta || !scale)
     return fail(X3_EINVAL, "null weight/bias/gamma/beta/scale pointer");
@@ -287,7 +333,7 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   if (!std::isfinite(lo) || !std::isfinite(hi) || lo > hi)
     return fail(X3_EINVAL, "clamp bounds must be finite with lo <= hi");
   if (B == 0) return X3_OK;
-  const size_t need = gn_workspace(s, groups, pool_k);
+  const size_t need = gn_workspace(s, groups, pool_k, nhwc);
   if (!workspace || workspace_bytes < need)
     return fail(X3_EWORKSPACE, "workspace of %zu bytes needed, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -332,7 +378,12 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   a.Ph = Ph;
   a.Pw = Pw;
   a.groups = groups;
-  rc = x3i::launch_gn_pool(a, st);
+  rc = nhwc ? x3i::launch_nhwc(a,
+                               x3i::gn_partials_per_channel(Cout, groups)
+                                   ? x3::EPI_GN_POOL_CH
+                                   : x3::EPI_GN_POOL,
+                               st)
+            : x3i::launch_gn_pool(a, st);
   if (rc != X3_OK) return rc;
 
   x3::GnFinArgs f{};
@@ -343,13 +394,47 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   f.out = out;
   f.groups = groups;
   f.cpg = Cout / groups;
-  f.pps = x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups);
+  f.C = Cout;
+  f.pps = gn_parts(s, groups, nhwc);
   f.plane = Ph * Pw;
   f.eps = eps;
   f.lo = lo;
   f.hi = hi;
   f.count = (double)f.cpg * s.Ho * s.Wo;
-  return x3i::launch_gn_finalize(f, B * groups, st);
+  return nhwc ? x3i::launch_gn_finalize_nhwc(f, B, st)
+              : x3i::launch_gn_finalize(f, B * groups, st);
+}
+}  // namespace
+
+X3_API size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W,
+                                            int Cout, int groups, int pool_k) {
+  return gn_workspace_query(B, Cin, H, W, Cout, groups, pool_k, false);
+}
+
+X3_API size_t x3_conv3x3_gn_nhwc_workspace_bytes(int B, int Cin, int H, int W,
+                                                 int Cout, int groups,
+                                                 int pool_k) {
+  return gn_workspace_query(B, Cin, H, W, Cout, groups, pool_k, true);
+}
+
+X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
+    const float* x, const float* w, const float* b, const float* gamma,
+    const float* beta, const float* scale, int groups, float eps, int pool_k,
+    float lo, float hi, float* out, void* workspace, size_t workspace_bytes,
+    int B, int Cin, int H, int W, int Cout, void* stream) {
+  return gn_entry(x, w, b, gamma, beta, scale, groups, eps, pool_k, lo, hi,
+                  out, workspace, workspace_bytes, B, Cin, H, W, Cout, stream,
+                  false);
+}
+
+X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_nhwc_f32(
+    const float* x, const float* w, const float* b, const float* gamma,
+    const float* beta, const float* scale, int groups, float eps, int pool_k,
+    float lo, float hi, float* out, void* workspace, size_t workspace_bytes,
+    int B, int Cin, int H, int W, int Cout, void* stream) {
+  return gn_entry(x, w, b, gamma, beta, scale, groups, eps, pool_k, lo, hi,
+                  out, workspace, workspace_bytes, B, Cin, H, W, Cout, stream,
+                  true);
 }
 
 // ============================================================================
