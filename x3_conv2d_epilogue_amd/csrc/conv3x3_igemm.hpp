@@ -106,7 +106,7 @@ constexpr int kMaxCout = 1024;
 
 // Compile-time geometry of one kernel configuration.
 template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_, bool X4_,
-          bool RESW_ = false, bool NHWC_ = false>
+          int RC_ = 0, bool NHWC_ = false>
 struct Geo {
   static constexpr int MT = MT_;          // 32-channel MFMA blocks per pass
   static constexpr int CC = CC_;          // input channels per K chunk
@@ -116,9 +116,11 @@ struct Geo {
   // Input rows are 16-byte aligned in memory (W % 4 == 0): stage the input
   // with 16-byte-per-lane loads (4x fewer load instructions).
   static constexpr bool X4 = X4_;
-  // The weight tile stays resident in LDS for the whole kernel (only valid
-  // when K fits one chunk, Cin <= CC); items then stage the input only.
-  static constexpr bool RESW = RESW_;
+  // RC > 0: the weight tiles of all K chunks (at most RC of them, one
+  // channel block) stay resident in LDS for the whole kernel; items then
+  // stage the input only.
+  static constexpr int RC = RC_;
+  static constexpr bool RESW = RC > 0;
   // x (and the per-channel outputs) in NHWC order: the input tile is staged
   // pixel-major, [XROWS][XCOLS][CCP], CCP = CC + 2.  With a pitch of 2 mod 4
   // dwords per pixel, the 32 pixels x 2 adjacent channels of a B-fragment
@@ -152,7 +154,7 @@ struct Geo {
   static constexpr int NBI = (NBX + NWAVE - 1) / NWAVE;   // per wave
   static constexpr int NBW = (NBWT + NWAVE - 1) / NWAVE;  // per wave
   static constexpr int STAGE = XBUF + (RESW ? 0 : WBUF);
-  static constexpr int LDS_DWORDS = 2 * STAGE + (RESW ? WBUF : 0);
+  static constexpr int LDS_DWORDS = 2 * STAGE + RC * WBUF;
   // blocks each wave stages per item
   static constexpr int NB_ITEM = NBI + (RESW ? 0 : NBW);
   static constexpr int KS = KC / 2;       // MFMA k-steps per chunk
@@ -256,7 +258,7 @@ __global__ void __launch_bounds__(G::NTHR)
   // other, so no wait is needed between them inside the MFMA loop.
   __shared__ float lds0[G::STAGE];
   __shared__ float lds1[G::STAGE];
-  __shared__ float ldsw[G::RESW ? G::WBUF : 1];  // resident weight tile
+  __shared__ float ldsw[G::RESW ? G::RC * G::WBUF : 1];  // resident weights
   // Per-channel constants of all ncb*COUT (padded) channels, loaded once:
   // bias, and the epilogue's channel parameter (multiplier, or for the
   // pooling path the direction flag 1 = keep the window maximum, 0 = keep
@@ -335,6 +337,7 @@ __global__ void __launch_bounds__(G::NTHR)
     int col_lim;   // local columns < col_lim are needed and real
     int kk_lim;    // weight columns < kk_lim are real
     int wbase;     // element offset of (co0, ci0) in the weight tensor
+    int wslot;     // resident weights: the chunk's slot in ldsw
   };
   const int HW = a.H * a.W, CinK = a.Cin * 9;
   auto lim_of = [&](const Item& it) X3_INLINE {
@@ -355,6 +358,7 @@ __global__ void __launch_bounds__(G::NTHR)
     const int kl = 9 * (a.Cin - it.ci0);
     l.kk_lim = kl < G::KC ? kl : G::KC;
     l.wbase = it.co0 * CinK + it.ci0 * 9;
+    l.wslot = 0;
     return l;
   };
   // Wave-local block i (compile-time) of the stage at `sbase`.  `zz` is an
@@ -420,7 +424,8 @@ __global__ void __launch_bounds__(G::NTHR)
       const uint32_t off =
           ((co * (uint32_t)CinK + (uint32_t)l.wbase + kk) << 2) |
           ((uint32_t)!ok << 31);
-      X3_LDS float* wdst = G::RESW ? (X3_LDS float*)ldsw : sbase + G::XBUF;
+      X3_LDS float* wdst =
+          G::RESW ? (X3_LDS float*)ldsw + l.wslot * G::WBUF : sbase + G::XBUF;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           w_rsrc, (X3_LDS void*)(wdst + blk * 64), 4, off, 0, 0, 0);
     }
@@ -822,8 +827,8 @@ __global__ void __launch_bounds__(G::NTHR)
         G::NHWC ? cur + (wm.row0 * G::XCOLS + wm.strip * 32 + l32) * G::CCP + h
                 : cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
     const X3_LDS float* ws =
-        (G::RESW ? (const X3_LDS float*)ldsw : cur + G::XBUF) + l32 * G::WP +
-        h * 9;
+        (G::RESW ? (const X3_LDS float*)ldsw + chunk * G::WBUF
+                 : cur + G::XBUF) + l32 * G::WP + h * 9;
     // Software pipeline over the k-steps of the chunk: step s issues the LDS
     // fragment reads of step s+1, its share of the next item's staging
     // loads, then its MFMAs; a scheduling fence keeps that order, so each
@@ -886,10 +891,21 @@ __global__ void __launch_bounds__(G::NTHR)
 #pragma unroll
     for (int i = 0; i < NB_W; ++i) issue(l0, (X3_LDS float*)lds0, i, 0);
     if constexpr (G::RESW) {
-      // the resident weight tile, once (K is a single chunk: ci0 = 0)
+      // the resident weight tiles, once: chunk c's K columns into slot c
+      // (one channel block, so co0 = 0)
 #pragma unroll
-      for (int i = G::NBI; i < G::NBI + G::NBW; ++i)
-        issue(l0, (X3_LDS float*)lds0, i, 0);
+      for (int c = 0; c < G::RC; ++c) {
+        if (c < a.nchunk) {
+          Lim lc = l0;
+          lc.wbase = c * G::CC * 9;
+          const int kl = 9 * (a.Cin - c * G::CC);
+          lc.kk_lim = kl < G::KC ? kl : G::KC;
+          lc.wslot = c;
+#pragma unroll
+          for (int i = G::NBI; i < G::NBI + G::NBW; ++i)
+            issue(lc, (X3_LDS float*)lds0, i, 0);
+        }
+      }
     }
   }
 #pragma unroll 1

@@ -52,8 +52,8 @@ x3_status run_conv(x3::ConvArgs a, hipStream_t st) {
   if (ncb * G::COUT * a.Cin * 9 * 4 >= (1ll << 31))
     return fail(X3_EUNSUPPORTED, "weights padded to whole channel blocks "
                 "must stay below 2 GiB");
-  // a resident weight tile needs a single (channel block, K chunk) pair
-  if (G::RESW && (ncb != 1 || nchunk != 1))
+  // resident weights: one channel block, at most RC K chunks
+  if (G::RESW && (ncb != 1 || nchunk > G::RC))
     return fail(X3_EUNSUPPORTED, "resident-weight configuration misapplied");
   // one workgroup per CU resident (two for the 4-wave configurations)
   const int cus = num_cus() * (G::NWAVE == 4 ? 2 : 1);
@@ -94,10 +94,31 @@ x3_status dispatch_mt4(const x3::ConvArgs& a, hipStream_t st) {
   return run_conv<x3::Geo<4, 8, 16, 1, 8, X4>, EPI>(a, st);
 }
 
+// The same tiles with the weights of (up to) two K chunks resident in LDS:
+// Cin <= 16 and one channel block (Cout <= 64 or 128).  16-byte staging only.
+template <int EPI>
+x3_status dispatch_mt2_rw(const x3::ConvArgs& a, hipStream_t st) {
+  if (a.Wo > 128) return run_conv<x3::Geo<2, 8, 4, 8, 8, true, 2>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8, true, 2>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8, true, 2>, EPI>(a, st);
+  return run_conv<x3::Geo<2, 8, 32, 1, 8, true, 2>, EPI>(a, st);
+}
+template <int EPI>
+x3_status dispatch_mt4_rw(const x3::ConvArgs& a, hipStream_t st) {
+  if (a.Wo > 128) return run_conv<x3::Geo<4, 8, 2, 8, 8, true, 2>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<4, 8, 4, 4, 8, true, 2>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<4, 8, 8, 2, 8, true, 2>, EPI>(a, st);
+  return run_conv<x3::Geo<4, 8, 16, 1, 8, true, 2>, EPI>(a, st);
+}
+
 template <int EPI>
 x3_status dispatch(const x3::ConvArgs& a, hipStream_t st) {
   const bool x4 = rows_aligned16(a);
-  if (channel_block_mt(a.Cout) == 4)
+  const int mt = channel_block_mt(a.Cout);
+  // resident weights when they fit: all K chunks of the one channel block
+  if (x4 && a.Cin <= 16 && a.Cout <= 32 * mt)
+    return mt == 4 ? dispatch_mt4_rw<EPI>(a, st) : dispatch_mt2_rw<EPI>(a, st);
+  if (mt == 4)
     return x4 ? dispatch_mt4<EPI, true>(a, st) : dispatch_mt4<EPI, false>(a, st);
   return x4 ? dispatch_mt2<EPI, true>(a, st) : dispatch_mt2<EPI, false>(a, st);
 }

@@ -28,9 +28,9 @@ GnGeo gn_geo(int Wo, int Cin, int Cout) {
 template <bool X4, int EPI>
 x3_status dispatch_gn(const x3::ConvArgs& a, hipStream_t st) {
   if (gn_resident(a.Cin, a.Cout)) {
-    if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 4, 4, 4, X4, true>, EPI>(a, st);
-    if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 8, 2, 4, X4, true>, EPI>(a, st);
-    return run_conv<x3::Geo<2, 8, 16, 1, 4, X4, true>, EPI>(a, st);
+    if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 4, 4, 4, X4, 1>, EPI>(a, st);
+    if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 8, 2, 4, X4, 1>, EPI>(a, st);
+    return run_conv<x3::Geo<2, 8, 16, 1, 4, X4, 1>, EPI>(a, st);
   }
   return dispatch_mt2<EPI, X4>(a, st);
 }

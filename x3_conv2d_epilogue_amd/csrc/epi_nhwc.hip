@@ -10,11 +10,11 @@ namespace x3i {
 namespace {
 
 template <int MT, int TH, int NCT>
-using GeoN = x3::Geo<MT, 8, TH, NCT, 8, false, false, true>;
+using GeoN = x3::Geo<MT, 8, TH, NCT, 8, false, 0, true>;
 // GroupNorm with Cin <= 8 and Cout <= 64: resident weights, two 4-wave
 // workgroups per CU, tiles of at most 64 columns (LDS: 78 KB each)
 template <int TH, int NCT>
-using GeoNR = x3::Geo<2, 8, TH, NCT, 4, false, true, true>;
+using GeoNR = x3::Geo<2, 8, TH, NCT, 4, false, 1, true>;
 
 bool gn_resident_nhwc(int Cin, int Cout) { return Cin <= 8 && Cout <= 64; }
 
