@@ -469,6 +469,61 @@ __global__ void __launch_bounds__(G::NTHR)
 #pragma unroll
   for (int j = 0; j < G::NW; ++j) run[j] = 0.0f;
 
+  // Deferred stores of the channel-min epilogues: a tile's epilogue parks
+  // its NW/2 results per lane here, and they are issued from the middle of
+  // the next item's MFMA loop.  Stores count in vmcnt, so storing them at
+  // once would make the wait for the next stage at the item start also wait
+  // for their completion.  A parked offset with bit 31 set is dropped, so
+  // the flush is unconditional.  (The GroupNorm epilogue stores at once:
+  // parking its results raised the register count past the budget.)
+  constexpr bool DEFER = EPI == EPI_MIN_TANH2 || EPI == EPI_SCALE_MIN;
+  constexpr bool IS_GN = EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH;
+  constexpr int NPEND = DEFER ? G::NW / 2 : 1;
+  constexpr uint32_t DROP = 0x80000000u;
+  uint32_t pend_v[NPEND], pend_off[NPEND];
+#pragma unroll
+  for (int k = 0; k < NPEND; ++k) {
+    pend_v[k] = 0u;
+    pend_off[k] = DROP;
+  }
+  int pend_n = 0;  // the parked results' sample (buffer resources rebuilt
+                   // at the flush: one register instead of eight)
+  // this sample's slice of out (and of the GroupNorm partials), as the
+  // epilogues address them
+  auto out_rsrc = [&](int n) X3_INLINE {
+    if constexpr (IS_GN)
+      return make_rsrc(a.out + (size_t)n * a.Cout * a.Ph * a.Pw,
+                       (uint32_t)(a.Cout * a.Ph * a.Pw * 4));
+    else
+      return make_rsrc(a.out + (size_t)n * a.Ho * a.Wo, (uint32_t)(a.Ho * a.Wo * 4));
+  };
+  auto part_rsrc = [&](int n) X3_INLINE {
+    const int pps = a.n_rt * a.n_ct * G::NWAVE;
+    const int rows = EPI == EPI_GN_POOL_CH ? a.Cout : a.groups;
+    return make_rsrc(a.part + (size_t)n * rows * pps, (uint32_t)(rows * pps * 16));
+  };
+  // Pin the parked values where the epilogue computed them: left free, the
+  // compiler may sink their computation to the flush in the next item and
+  // keep the old accumulators alive across it.
+  auto pin_parked = [&]() X3_INLINE {
+#pragma unroll
+    for (int k = 0; k < NPEND; ++k) {
+      asm volatile("" : "+v"(pend_v[k]));
+      asm volatile("" : "+v"(pend_off[k]));
+    }
+  };
+  auto flush = [&]() X3_INLINE {
+    if constexpr (DEFER) {
+      const __amdgpu_buffer_rsrc_t o_rsrc = out_rsrc(pend_n);
+#pragma unroll
+      for (int k = 0; k < NPEND; ++k) {
+        __builtin_amdgcn_raw_buffer_store_b32(pend_v[k], o_rsrc, pend_off[k],
+                                              0, 0);
+        pend_off[k] = DROP;
+      }
+    }
+  };
+
   auto epilogue = [&](int t, int cb) X3_INLINE {
     // ---- epilogue for channel block cb of tile t ------------------------------
     const int co0 = cb * G::COUT;
@@ -487,8 +542,6 @@ __global__ void __launch_bounds__(G::NTHR)
       static_assert(G::NW % 2 == 0, "lane halves split the N-tiles");
       constexpr int HN = G::NW / 2;
       const bool use_max = (EPI == EPI_SCALE_MIN) && !(a.s0 >= 0.0f);
-      const __amdgpu_buffer_rsrc_t o_rsrc =
-          make_rsrc(a.out + (size_t)n * a.Ho * a.Wo, (uint32_t)(a.Ho * a.Wo * 4));
       float m[G::NW];
 #pragma unroll
       for (int j = 0; j < G::NW; ++j) {
@@ -521,12 +574,14 @@ __global__ void __launch_bounds__(G::NTHR)
           y = tanhf(tanhf(v));
         else
           y = a.s0 * v;
-        // bounded store into this sample's output plane; bit 31 drops it
-        const uint32_t off = ((uint32_t)(r * a.Wo + c) << 2) |
-                             ((uint32_t)!(col_ok && r < a.Ho) << 31);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y),
-                                              o_rsrc, off, 0, 0);
+        // bounded store into this sample's output plane (parked for the
+        // next item's loop); bit 31 drops it
+        pend_v[jj] = __builtin_bit_cast(uint32_t, y);
+        pend_off[jj] = ((uint32_t)(r * a.Wo + c) << 2) |
+                       ((uint32_t)!(col_ok && r < a.Ho) << 31);
       }
+      pend_n = n;
+      pin_parked();
     } else if constexpr (EPI == EPI_MUL_LRELU_GELU ||
                          EPI == EPI_MUL_LRELU_GELU_TANH || EPI == EPI_STORE) {
       const float slope = a.s0;
@@ -600,14 +655,13 @@ __global__ void __launch_bounds__(G::NTHR)
     } else {  // EPI_GN_POOL(_CH): requires NW == 4 and pool 4
       static_assert(G::NW == 4, "pool needs 4 rows");
       // Stores go through raw buffer resources over this sample's slice of
-      // `part` and `out`; a store that must not happen gets bit 31 set in
-      // its offset (past num_records, dropped by the hardware), so the
-      // epilogue has no exec-masked branches.
+      // `part` and `out` (out_rsrc, part_rsrc); a store that must not happen
+      // gets bit 31 set in its offset (past num_records, dropped by the
+      // hardware), so the epilogue has no exec-masked branches.  Padded
+      // channels and groups land past the ends and are dropped.
       const int PP = a.Ph * a.Pw;
       const int pps = a.n_rt * a.n_ct * G::NWAVE;
-      // (padded channels and groups land past the ends and are dropped)
-      const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(
-          a.out + (size_t)n * a.Cout * PP, (uint32_t)(a.Cout * PP * 4));
+      const __amdgpu_buffer_rsrc_t o_rsrc = out_rsrc(n);
       // (1) GroupNorm partials of this wave: per group, the count, the sum
       // and the sum of squared deviations from the wave's own group mean,
       // over the wave's valid pixels.  A group is 4 consecutive channels,
@@ -621,9 +675,6 @@ __global__ void __launch_bounds__(G::NTHR)
       ncol_ok = ncol_ok < 0 ? 0 : (ncol_ok > 32 ? 32 : ncol_ok);
       const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
       if constexpr (EPI == EPI_GN_POOL) {
-      const __amdgpu_buffer_rsrc_t p_rsrc =
-          make_rsrc(a.part + (size_t)n * a.groups * pps,
-                    (uint32_t)(a.groups * pps * 16));
       const float cnt = (float)(4 * nrow_ok * ncol_ok);
       const float inv_cnt = cnt > 0.0f ? 1.0f / cnt : 0.0f;
       float my_sum = 0.0f, my_m2 = 0.0f;  // lane l32 = mt*4+q keeps (mt, q)
@@ -656,7 +707,7 @@ __global__ void __launch_bounds__(G::NTHR)
                              ((uint32_t)(l32 >= G::MT * 4) << 31);
         const float4 v = make_float4(my_sum, my_m2, cnt, 0.0f);
         __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(u32x4, v), p_rsrc, off, 0, 0);
+            __builtin_bit_cast(u32x4, v), part_rsrc(n), off, 0, 0);
       }
       } else {
       // (1') Per-channel partials (any group size; the finalize merges the
@@ -670,9 +721,7 @@ __global__ void __launch_bounds__(G::NTHR)
       // half-row mirror) and the keep decision is lane bit 4, 3, 2; two
       // quad steps (l^1, l^2) complete the sums.  Each quad ends with
       // element (l32 >> 2) & 7 of the 8, and its first lane stores it.
-      const __amdgpu_buffer_rsrc_t p_rsrc =
-          make_rsrc(a.part + (size_t)n * a.Cout * pps,
-                    (uint32_t)(a.Cout * pps * 16));
+      const __amdgpu_buffer_rsrc_t p_rsrc = part_rsrc(n);
       const float cnt = (float)(nrow_ok * ncol_ok);
       const float inv_cnt = cnt > 0.0f ? 1.0f / cnt : 0.0f;
       const bool b4 = (l32 >> 4) & 1, b3 = (l32 >> 3) & 1, b2 = (l32 >> 2) & 1;
@@ -857,6 +906,9 @@ __global__ void __launch_bounds__(G::NTHR)
         for (int u = 0; u < BPS; ++u)
           if (s * BPS + u < NB_W) issue(nl, nxt, s * BPS + u, zz);
       }
+      // the previous tile's parked epilogue stores, once the staging loads
+      // are out
+      if (s == KS_ISSUE) flush();
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -914,6 +966,7 @@ __global__ void __launch_bounds__(G::NTHR)
     if (item + 1 < nitems)
       run_item(std::integral_constant<int, 1>{}, item + 1, pos);
   }
+  flush();  // the last tile's parked stores
   // the last item's (unused) prefetch must land before the LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
