@@ -108,13 +108,17 @@ def test_nhwc_gn_pool(shape, cg):
 
 def test_nhwc_matches_nchw_on_full_width_shape():
     """One larger shape through both layouts: identical inputs, results
-    within the parity bar of each other (their summation orders match)."""
+    within fp32 rounding of each other (the two layouts sum the K terms in
+    different orders), and both within the parity bar of the oracle."""
     d = random_case("mul_lrelu_gelu", 2, 16, 40, 258, 64, seed=1900)
     g = {k: v.to(DEV) for k, v in d.items()}
     gc = dev_cl(d)
     a = x3.conv3x3_min_tanh2(g["x"], g["weight"], g["bias"])
     b = x3.conv3x3_min_tanh2(gc["x"], gc["weight"], gc["bias"])
-    assert torch.equal(a, b)
+    assert (a - b).abs().max().item() <= 2e-6
     a = x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"])
     b = x3.conv3x3_mul_lrelu_gelu(gc["x"], gc["weight"], gc["bias"], gc["multiplier"])
-    assert torch.equal(a, b.contiguous())
+    assert (a - b.contiguous()).abs().max().item() <= 2e-6
+    n = {k: v.numpy() for k, v in d.items()}
+    close(b, oracle.mul_lrelu_gelu(n["x"], n["weight"], n["bias"], n["multiplier"], 0.01),
+          "gelu 258")

@@ -133,24 +133,39 @@ struct Geo {
   static constexpr int XROWS = TH + 2;    // input rows per tile (halo)
   static constexpr int XCOLS = TWC + 2;   // input columns per tile (halo)
   static constexpr int XP = (XCOLS + 3) / 4 * 4;  // LDS row pitch (dwords)
-  // LDS channel stride: >= XROWS*XP and == 32 (mod 64) dwords, so the two
-  // lane halves of a B-fragment read (channels ci and ci+1) use disjoint
-  // banks.
+  // K order inside a chunk.
+  //  * KO (the 16-byte configurations, NCHW): k-step s = 0..KS-1 and lane
+  //    half h take K index s + KS*h, i.e. channel s/9 + CC/2*h at tap s%9.
+  //    A lane's weights for 4 consecutive k-steps are then 4 consecutive
+  //    floats of its weight row (one ds_read_b128), and weight rows are
+  //    staged with 16-byte loads (pitch WP = 76: 16-byte aligned rows, and
+  //    76 = 12 mod 64 puts 16 consecutive rows in 16 disjoint 4-bank
+  //    groups).  The input channel stride CS = 8 mod 16 makes the two
+  //    halves' channels (CC/2 = 4 apart) fall in opposite bank halves.
+  //  * otherwise: k-step s = tap*(CC/2) + cp, lane half h takes channel
+  //    2*cp + h; channel stride CS = 32 mod 64 (opposite bank halves for
+  //    adjacent channels), odd weight pitch WP = KC + 1 (conflict-free
+  //    4-byte reads).
+  static constexpr bool KO = X4 && !NHWC;
   static constexpr int CS0 = XROWS * XP;
-  static constexpr int CS = CS0 + ((32 - (CS0 % 64)) + 64) % 64;
-  static constexpr int XBUF =             // input dwords per stage
-      NHWC ? (XROWS * XCOLS * CCP + 63) / 64 * 64 : CC * CS;
+  static constexpr int CS =
+      KO ? CS0 + ((8 - (CS0 % 16)) + 16) % 16
+         : CS0 + ((32 - (CS0 % 64)) + 64) % 64;
   static constexpr int KC = 9 * CC;       // K per chunk
-  static constexpr int WP = KC + 1;       // odd weight-row pitch: conflict-free
+  static constexpr int XBLK = X4 ? 256 : 64;
+  static constexpr int XBUF =             // input dwords per stage
+      NHWC ? (XROWS * XCOLS * CCP + 63) / 64 * 64
+           : (CC * CS + XBLK - 1) / XBLK * XBLK;
+  static constexpr int WP = KO ? KC + 4 : KC + 1;  // weight-row pitch
   static constexpr int WBUF = COUT * WP;  // weight dwords per stage
   // Staging blocks: the input region is filled in blocks of 256 dwords
   // (16 bytes per lane, X4) or 64 dwords (4 bytes per lane), the weight
-  // region in blocks of 64 dwords.  Every wavefront issues the same number
+  // region likewise (256 with KO).  Every wavefront issues the same number
   // of blocks, NBI + NBW per item; a wavefront whose turn runs past the
   // last block reloads the last block (same data to the same place).
-  static constexpr int XBLK = X4 ? 256 : 64;
+  static constexpr int WBLK = KO ? 256 : 64;
   static constexpr int NBX = XBUF / XBLK;                 // input blocks
-  static constexpr int NBWT = WBUF / 64;                  // weight blocks
+  static constexpr int NBWT = WBUF / WBLK;                // weight blocks
   static constexpr int NBI = (NBX + NWAVE - 1) / NWAVE;   // per wave
   static constexpr int NBW = (NBWT + NWAVE - 1) / NWAVE;  // per wave
   static constexpr int STAGE = XBUF + (RESW ? 0 : WBUF);
@@ -164,7 +179,9 @@ struct Geo {
   static_assert(CC % 2 == 0, "CC must be even");
   static_assert(!NHWC || (CC % 4 == 0 && !X4),
                 "NHWC: CC % 4 == 0 (pitch 2 mod 4), 4-byte staging");
-  static_assert(XBUF % XBLK == 0 && WBUF % 64 == 0, "whole staging blocks");
+  static_assert(XBUF % XBLK == 0 && WBUF % WBLK == 0, "whole staging blocks");
+  static_assert(!KO || (CC == 8 && KS % 4 == 0 && (CC / 2 * CS) % 64 == 32),
+                "KO: 8-channel chunks, halves in opposite bank halves");
   static_assert(NTILE_N % NWAVE == 0, "N-tiles must split evenly over waves");
   static_assert(TH % NW == 0, "a wave's N-tiles must lie in one strip");
   static_assert(LDS_DWORDS * 4 + 2 * kMaxCout * 4 <= 160 * 1024,
@@ -256,9 +273,11 @@ __global__ void __launch_bounds__(G::NTHR)
   // Two LDS stages as two separate arrays: the direct-to-LDS loads that
   // fill one stage are then visibly disjoint from the fragment reads of the
   // other, so no wait is needed between them inside the MFMA loop.
-  __shared__ float lds0[G::STAGE];
-  __shared__ float lds1[G::STAGE];
-  __shared__ float ldsw[G::RESW ? G::RC * G::WBUF : 1];  // resident weights
+  // (16-byte aligned: direct-to-LDS 16-byte staging, ds_read_b128)
+  __shared__ __attribute__((aligned(16))) float lds0[G::STAGE];
+  __shared__ __attribute__((aligned(16))) float lds1[G::STAGE];
+  __shared__ __attribute__((aligned(16)))
+  float ldsw[G::RESW ? G::RC * G::WBUF : 1];  // resident weights
   // Per-channel constants of all ncb*COUT (padded) channels, loaded once:
   // bias, and the epilogue's channel parameter (multiplier, or for the
   // pooling path the direction flag 1 = keep the window maximum, 0 = keep
@@ -403,7 +422,10 @@ __global__ void __launch_bounds__(G::NTHR)
       const uint32_t rem = p - cil * G::CS;
       const uint32_t row = rem / G::XP;
       const uint32_t col = rem - row * G::XP;
+      // (KO rounds the stage up to whole blocks: slots past CC channels
+      // are padding)
       const bool ok = (cil < (uint32_t)l.ci_lim) &
+                      (!G::KO || cil < (uint32_t)G::CC) &
                       (row < (uint32_t)l.row_lim) &
                       (col < (uint32_t)l.col_lim);
       const uint32_t off =
@@ -417,7 +439,11 @@ __global__ void __launch_bounds__(G::NTHR)
     } else {
       int blk = wave + zz + (i - G::NBI) * G::NWAVE;
       blk = blk < G::NBWT - 1 ? blk : G::NBWT - 1;
-      const uint32_t q = (uint32_t)(blk * 64 + lane);
+      // KO: lane l moves 4 consecutive floats of one weight row (the pitch
+      // and the row's K columns are multiples of 4; the dispatch keeps
+      // Cin % 4 == 0 so the global rows are 16-byte aligned too).  Columns
+      // past the chunk's K (and the row padding) read as zero.
+      const uint32_t q = (uint32_t)(blk * G::WBLK + lane * (G::WBLK / 64));
       const uint32_t co = q / G::WP;
       const uint32_t kk = q - co * G::WP;
       const bool ok = kk < (uint32_t)l.kk_lim;
@@ -426,8 +452,11 @@ __global__ void __launch_bounds__(G::NTHR)
           ((uint32_t)!ok << 31);
       X3_LDS float* wdst =
           G::RESW ? (X3_LDS float*)ldsw + l.wslot * G::WBUF : sbase + G::XBUF;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          w_rsrc, (X3_LDS void*)(wdst + blk * 64), 4, off, 0, 0, 0);
+      X3_LDS void* dst = (X3_LDS void*)(wdst + blk * G::WBLK);
+      if constexpr (G::KO)
+        lds_load_x4(w_rsrc, dst, off);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 4, off, 0, 0, 0);
     }
   };
   // blocks per wave per item, BPS per k-step over the first half of the
@@ -874,30 +903,52 @@ __global__ void __launch_bounds__(G::NTHR)
 
     const X3_LDS float* xs =
         G::NHWC ? cur + (wm.row0 * G::XCOLS + wm.strip * 32 + l32) * G::CCP + h
+        : G::KO ? cur + h * (G::CC / 2) * G::CS + wm.row0 * G::XP +
+                      wm.strip * 32 + l32
                 : cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
     const X3_LDS float* ws =
         (G::RESW ? (const X3_LDS float*)ldsw + chunk * G::WBUF
-                 : cur + G::XBUF) + l32 * G::WP + h * 9;
+                 : cur + G::XBUF) + l32 * G::WP + h * (G::KO ? G::KS : 9);
     // Software pipeline over the k-steps of the chunk: step s issues the LDS
     // fragment reads of step s+1, its share of the next item's staging
     // loads, then its MFMAs; a scheduling fence keeps that order, so each
     // MFMA's operands were requested a full step (MT*NW MFMAs) earlier.
+    // KO reads the weights of 4 k-steps at once, a group ahead.
     float av[2][G::MT], bv[2][G::NW];
-    auto load_frag = [&](int s, float (&A)[G::MT], float (&Bv)[G::NW]) X3_INLINE {
-      const int tap = s / (G::CC / 2);
-      const int cp = s % (G::CC / 2);
-      const int kh = tap / 3, kw = tap % 3;
+    f32x4 a4[2][G::KO ? G::MT : 1];
+    auto load_a4 = [&](int g, f32x4 (&A)[G::KO ? G::MT : 1]) X3_INLINE {
 #pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
-        A[mt] = ws[mt * 32 * G::WP + cp * 18 + tap];
-#pragma unroll
-      for (int j = 0; j < G::NW; ++j)
-        Bv[j] = G::NHWC ? xs[((j + kh) * G::XCOLS + kw) * G::CCP + 2 * cp]
-                        : xs[2 * cp * G::CS + (j + kh) * G::XP + kw];
+      for (int mt = 0; mt < (G::KO ? G::MT : 1); ++mt)
+        A[mt] = *reinterpret_cast<const X3_LDS f32x4*>(ws + mt * 32 * G::WP +
+                                                       4 * g);
     };
+    auto load_frag = [&](int s, float (&A)[G::MT], float (&Bv)[G::NW]) X3_INLINE {
+      if constexpr (G::KO) {
+        const int ci = s / 9, tap = s % 9, kh = tap / 3, kw = tap % 3;
+#pragma unroll
+        for (int j = 0; j < G::NW; ++j)
+          Bv[j] = xs[ci * G::CS + (j + kh) * G::XP + kw];
+      } else {
+        const int tap = s / (G::CC / 2);
+        const int cp = s % (G::CC / 2);
+        const int kh = tap / 3, kw = tap % 3;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+          A[mt] = ws[mt * 32 * G::WP + cp * 18 + tap];
+#pragma unroll
+        for (int j = 0; j < G::NW; ++j)
+          Bv[j] = G::NHWC ? xs[((j + kh) * G::XCOLS + kw) * G::CCP + 2 * cp]
+                          : xs[2 * cp * G::CS + (j + kh) * G::XP + kw];
+      }
+    };
+    if constexpr (G::KO) load_a4(0, a4[0]);
     load_frag(0, av[0], bv[0]);
 #pragma unroll
     for (int s = 0; s < G::KS; ++s) {
+      if constexpr (G::KO) {
+        if (s % 4 == 0 && s / 4 + 1 < G::KS / 4)
+          load_a4(s / 4 + 1, a4[(s / 4 + 1) & 1]);
+      }
       if (s + 1 < G::KS) load_frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
       // (unconditional: on the last item this reloads the current item's
       // data into the idle stage, which keeps the step free of branches)
@@ -914,7 +965,8 @@ __global__ void __launch_bounds__(G::NTHR)
 #pragma unroll
         for (int j = 0; j < G::NW; ++j)
           acc[mt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-              av[s & 1][mt], bv[s & 1][j], acc[mt][j], 0, 0, 0);
+              G::KO ? a4[(s / 4) & 1][mt][s % 4] : av[s & 1][mt],
+              bv[s & 1][j], acc[mt][j], 0, 0, 0);
       // Issue order inside the step: each MFMA (64 cycles in the matrix
       // core) is followed by a slice of this wave's other work -- LDS
       // fragment reads, staging address arithmetic, one staging load -- so

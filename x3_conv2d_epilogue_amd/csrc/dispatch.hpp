@@ -31,11 +31,13 @@ inline int padded_cout(int Cout) {
   return (Cout + cb - 1) / cb * cb;
 }
 
-// Input rows are 16-byte aligned when W % 4 == 0 (x itself comes from the
-// caller's allocator, checked for 16-byte alignment): then the input is
-// staged with 16-byte loads.
+// The 16-byte configurations stage input rows and weight rows with 16-byte
+// loads: input rows are 16-byte aligned when W % 4 == 0 (x itself comes
+// from the caller's allocator, checked for 16-byte alignment), weight rows
+// when Cin % 4 == 0.
 inline bool rows_aligned16(const x3::ConvArgs& a) {
-  return (a.W % 4 == 0) && (((uintptr_t)a.x & 15u) == 0);
+  return (a.W % 4 == 0) && (a.Cin % 4 == 0) && (((uintptr_t)a.x & 15u) == 0) &&
+         (((uintptr_t)a.w & 15u) == 0);
 }
 
 template <class G, int EPI>
