@@ -572,16 +572,25 @@ __global__ void __launch_bounds__(G::NTHR)
       constexpr int HN = G::NW / 2;
       const bool use_max = (EPI == EPI_SCALE_MIN) && !(a.s0 >= 0.0f);
       float m[G::NW];
+      // (one uniform branch around two compile-time reductions, rather than
+      // a min, a max and a select per element)
+      auto reduce = [&](auto maxc) X3_INLINE {
+        constexpr bool MX = decltype(maxc)::value;
 #pragma unroll
-      for (int j = 0; j < G::NW; ++j) {
-        float v = acc[0][j][0];
+        for (int j = 0; j < G::NW; ++j) {
+          float v = acc[0][j][0];
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
+          for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            v = use_max ? fmaxf(v, acc[mt][j][i]) : fminf(v, acc[mt][j][i]);
-        m[j] = v;
-      }
+            for (int i = 0; i < 16; ++i)
+              v = MX ? fmaxf(v, acc[mt][j][i]) : fminf(v, acc[mt][j][i]);
+          m[j] = v;
+        }
+      };
+      if (use_max)
+        reduce(std::true_type{});
+      else
+        reduce(std::false_type{});
       if (a.ncb > 1) {  // (uniform) fold in the earlier blocks' extremum
         const bool first = cb == 0;
 #pragma unroll
