@@ -86,9 +86,13 @@ def test_epi_mul_lrelu_gelu_both_forms(shape):
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 7])
 @pytest.mark.parametrize("cg", [(16, 4), (12, 3), (8, 8), (6, 1)])
-def test_epi_gn_any_pool(k, cg):
+@pytest.mark.parametrize("hw", [(23, 29), (22, 30), (13, 260)])
+def test_epi_gn_any_pool(k, cg, hw):
+    """Odd and even row lengths (even rows with 4x4 windows take the 8-byte
+    row-span kernel), one and several 128-column spans, remainder rows and
+    columns outside the last window."""
     C, groups = cg
-    shape = (2, C, 23, 29)
+    shape = (2, C) + hw
     say(f"epi gn {shape} groups={groups} k={k}")
     y, x, w, b = identity_case(*shape, seed=200 + k + C)
     g = torch.Generator().manual_seed(k)

@@ -74,7 +74,9 @@ x3_status launch_epi_gn(const x3::GnPlaneArgs& g, int64_t B, int groups,
   if (planes >= (1ll << 31) || B * groups >= (1ll << 31))
     return fail(X3_EUNSUPPORTED, "too many planes for one launch");
   const dim3 grid((unsigned)planes), block(x3::kEpiThreads);
-  if (g.k == 4)
+  if (g.k == 4 && g.W % 2 == 0 && ((uintptr_t)g.y & 7u) == 0)
+    hipLaunchKernelGGL((x3::gn_plane_k4w2_kernel<4>), grid, block, 0, st, g);
+  else if (g.k == 4)
     hipLaunchKernelGGL((x3::gn_plane_kernel<4>), grid, block, 0, st, g);
   else
     hipLaunchKernelGGL((x3::gn_plane_kernel<0>), grid, block, 0, st, g);

@@ -363,4 +363,95 @@ __global__ void __launch_bounds__(kEpiThreads) gn_plane_kernel(const GnPlaneArgs
   }
 }
 
+// The same operation for 4x4 windows and an even row length: lanes take 2
+// adjacent columns each (8-byte loads), so one wavefront step covers 128
+// columns of 4 rows -- a whole row of 126 floats in one load instruction
+// -- and a window is 2 lanes.  Each step reads every column of its rows
+// (the columns right of the last window feed only the statistics); the
+// rows below the last window are read afterwards for the statistics.
+// (a template only so that every translation unit may include it)
+template <int K4 = 4>
+__global__ void __launch_bounds__(kEpiThreads) gn_plane_k4w2_kernel(const GnPlaneArgs a) {
+  constexpr int NT = kEpiThreads, NWV = NT / 64;
+  __shared__ double red0[NT / 64], red1[NT / 64];
+  const int64_t nc = blockIdx.x;  // n * C + c
+  const int c = (int)(nc % a.C);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.H * a.W, PP = a.Ph * a.Pw;
+  const float* yb = a.y + nc * (int64_t)P;
+  float* ob = a.out + nc * (int64_t)PP;
+  const bool keep_max = (a.gamma[c] >= 0.0f) == (a.scale[c] >= 0.0f);
+  const float Kf = yb[0];
+  float s1 = 0.0f, s2 = 0.0f;
+  const int cw = a.Pw * 4, rh = a.Ph * 4;
+  const int nsx = (a.W + 127) / 128;       // 128-column steps per row band
+  const int nunits = a.Ph * nsx;
+  constexpr int UNR = 4;
+  for (int u0 = wave; u0 < nunits; u0 += NWV * UNR) {
+    float2 v[UNR][4];
+    int pyq[UNR], xq[UNR];
+    bool okq[UNR];
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) {
+      const int u = u0 + q * NWV;
+      const int py = u / nsx;
+      const int x = (u - py * nsx) * 128 + 2 * lane;  // this lane's first column
+      pyq[q] = py;
+      xq[q] = x;
+      okq[q] = u < nunits && x < a.W;  // (W even: x + 1 < W too)
+      // (a unit past the end, or a lane past the row, reads the plane's
+      // first two columns instead: no load leaves the plane)
+      const float* src = yb + (okq[q] ? py * 4 * a.W + x : 0);
+#pragma unroll
+      for (int dy = 0; dy < 4; ++dy)
+        v[q][dy] = *reinterpret_cast<const float2*>(src + dy * a.W);
+    }
+#pragma unroll
+    for (int q = 0; q < UNR; ++q) {
+      const bool ok = okq[q];
+      float mx = -__builtin_inff(), mn = __builtin_inff();
+#pragma unroll
+      for (int dy = 0; dy < 4; ++dy) {
+        const float d0 = ok ? v[q][dy].x - Kf : 0.0f;
+        const float d1 = ok ? v[q][dy].y - Kf : 0.0f;
+        s1 += d0 + d1;
+        s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
+        mx = fmaxf(mx, fmaxf(v[q][dy].x, v[q][dy].y));
+        mn = fminf(mn, fminf(v[q][dy].x, v[q][dy].y));
+      }
+      // the 2 lanes of a window are an even/odd pair
+      mx = fmaxf(mx, quad_swap<0xB1>(mx));
+      mn = fminf(mn, quad_swap<0xB1>(mn));
+      const int x = xq[q];
+      if (ok && (lane & 1) == 0 && x + 3 < cw)
+        ob[pyq[q] * a.Pw + x / 4] = keep_max ? mx : mn;
+    }
+  }
+  // the rows below the last window, for the statistics (8-byte pairs)
+  const int half = a.W / 2;
+  const int rem = (a.H - rh) * half;
+  for (int e0 = tid; e0 < rem; e0 += 4 * NT) {
+    float2 w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + q * NT < rem ? e0 + q * NT : 0;
+      w[q] = *reinterpret_cast<const float2*>(yb + rh * a.W + 2 * e);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = e0 + q * NT < rem;
+      const float d0 = ok ? w[q].x - Kf : 0.0f, d1 = ok ? w[q].y - Kf : 0.0f;
+      s1 += d0 + d1;
+      s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
+    }
+  }
+  const double S1 = block_sum_d<NT>((double)s1, red0);
+  const double S2 = block_sum_d<NT>((double)s2, red1);
+  if (tid == 0) {
+    const double n = (double)P;
+    a.part[nc] = make_float4((float)(n * (double)Kf + S1),
+                             (float)fmax(S2 - S1 * S1 / n, 0.0), (float)n, 0.0f);
+  }
+}
+
 }  // namespace x3
