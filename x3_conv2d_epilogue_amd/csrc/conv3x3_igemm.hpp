@@ -223,11 +223,23 @@ enum : int {
   DPP_ROW_ROR4 = 0x124,  // rotate a row of 16 by 4
   DPP_ROW_ROR8 = 0x128   // rotate a row of 16 by 8
 };
+// (All of them stay inside a row, so no lane reads a disabled source; the
+// bound-control form needs no register for the unused `old` operand.)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                         0xF, 0xF, false));
+                                         0xF, 0xF, true));
+}
+// NaN-propagating maximum / minimum (v_maximum3_f32 / v_minimum3_f32 on
+// gfx950: two inputs per instruction in a chain, and no quieting of the
+// inputs, which fmaxf / fminf need in IEEE mode for values the compiler
+// cannot prove quiet, such as matrix-core results and lane permutations).
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float vmin(float a, float b) {
+  return __builtin_elementwise_minimum(a, b);
 }
 // Lane l <-> l ^ 16 inside each half-wave (ds_swizzle bit mode:
 // and_mask 0x1F, xor_mask 0x10).
@@ -280,12 +292,12 @@ __global__ void __launch_bounds__(G::NTHR)
   float ldsw[G::RESW ? G::RC * G::WBUF : 1];  // resident weights
   // Per-channel constants of all ncb*COUT (padded) channels, loaded once:
   // bias, and the epilogue's channel parameter (multiplier, or for the
-  // pooling path the direction flag 1 = keep the window maximum, 0 = keep
-  // the minimum).  Reading them from LDS keeps global loads out of the main
+  // pooling path the direction +1 = keep the window maximum, -1 = keep the
+  // minimum).  Reading them from LDS keeps global loads out of the main
   // loop, whose vmcnt waits would otherwise also wait for the next stage's
   // prefetch.
   __shared__ float s_bias[kMaxCout];
-  __shared__ float s_par[kMaxCout];
+  __shared__ __attribute__((aligned(16))) float s_par[kMaxCout];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -484,7 +496,7 @@ __global__ void __launch_bounds__(G::NTHR)
       if constexpr (EPI == EPI_MUL_LRELU_GELU || EPI == EPI_MUL_LRELU_GELU_TANH)
         pv = a.v0[co];
       if constexpr (EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH)
-        pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : 0.0f;
+        pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : -1.0f;
     }
     s_bias[co] = bv;
     s_par[co] = pv;
@@ -713,37 +725,83 @@ __global__ void __launch_bounds__(G::NTHR)
       ncol_ok = ncol_ok < 0 ? 0 : (ncol_ok > 32 ? 32 : ncol_ok);
       const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
       if constexpr (EPI == EPI_GN_POOL) {
+      static_assert(G::MT == 2, "8 groups per lane half");
       const float cnt = (float)(4 * nrow_ok * ncol_ok);
       const float inv_cnt = cnt > 0.0f ? 1.0f / cnt : 0.0f;
-      float my_sum = 0.0f, my_m2 = 0.0f;  // lane l32 = mt*4+q keeps (mt, q)
+      // shift of group gi = mt*4 + q: its first channel at the half's
+      // first pixel
+      f32x8 kv;
 #pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
+      for (int gi = 0; gi < 8; ++gi) kv[gi] = half_lane0(acc[gi >> 2][0][4 * (gi & 3)], h);
+      // in-lane sums over the lane's pixels: sv[2gi] = S1, sv[2gi+1] = S2
+      f32x16 sv;
+      auto lane_sums = [&](auto masked) X3_INLINE {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float K = half_lane0(acc[mt][0][4 * q], h);
+        for (int gi = 0; gi < 8; ++gi) {
+          const int mt = gi >> 2, q = gi & 3;
           float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
           for (int j = 0; j < G::NW; ++j) {
             const bool ok = col_ok && j < nrow_ok;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float d = ok ? acc[mt][j][4 * q + e] - K : 0.0f;
+              float d = acc[mt][j][4 * q + e] - kv[gi];
+              if constexpr (decltype(masked)::value) d = ok ? d : 0.0f;
               s1 += d;
               s2 = fmaf(d, d, s2);
             }
           }
-          s1 = sum32(s1);
-          s2 = sum32(s2);
-          const bool mine = l32 == mt * 4 + q;
-          my_sum = mine ? fmaf(K, cnt, s1) : my_sum;
-          my_m2 = mine ? fmaxf(s2 - s1 * s1 * inv_cnt, 0.0f) : my_m2;
+          sv[2 * gi] = s1;
+          sv[2 * gi + 1] = s2;
         }
+      };
+      // (uniform) whole wave tiles need no masks
+      if (nrow_ok == G::NW && ncol_ok == 32)
+        lane_sums(std::false_type{});
+      else
+        lane_sums(std::true_type{});
+      // Sums over the 32 lanes of a half by a halving exchange: in each
+      // step a lane keeps the half of its values selected by one lane bit,
+      // adds the partner's copy of that half and hands over the other
+      // half.  Bits 3, 2, 0, 1 (DPP partners l^8 by a row rotation, l^7 by
+      // the half-row mirror, then the quad), and finally l^16 for the one
+      // value left.  Lane bits (3, 2, 0) then name the group and bit 1
+      // whether the lane holds S1 or S2.
+      const bool b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1,
+                 b3 = (lane >> 3) & 1;
+      f32x8 r8 = b3 ? sv.hi : sv.lo;
       {
-        // lane (h, l32 = mt*4+q) writes group g = co0/4 + mt*8 + 2q + h
-        const int g = (co0 >> 2) + (l32 >> 2) * 8 + 2 * (l32 & 3) + h;
+        const f32x8 give = b3 ? sv.lo : sv.hi;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r8[k] += dpp<DPP_ROW_ROR8>(give[k]);
+      }
+      f32x4 r4 = b2 ? r8.hi : r8.lo;
+      {
+        const f32x4 give = b2 ? r8.lo : r8.hi;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r4[k] += dpp<DPP_ROW_HALF_MIRROR>(give[k]);
+      }
+      f32x2 r2 = b0 ? r4.hi : r4.lo;
+      {
+        const f32x2 give = b0 ? r4.lo : r4.hi;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) r2[k] += dpp<DPP_QUAD_XOR1>(give[k]);
+      }
+      float S = (b1 ? r2.y : r2.x) + dpp<DPP_QUAD_XOR2>(b1 ? r2.x : r2.y);
+      S += swz_xor16(S);
+      const float S1 = S, S2 = dpp<DPP_QUAD_XOR2>(S);  // (valid where !b1)
+      const int gi = 4 * b3 + 2 * b2 + b0;
+      const f32x4 k4 = b3 ? kv.hi : kv.lo;
+      const f32x2 k2 = b2 ? k4.hi : k4.lo;
+      const float K = b0 ? k2.y : k2.x;
+      {
+        // lanes with bits 1 and 4 clear store group
+        // g = co0/4 + mt*8 + 2q + h of gi = mt*4 + q
+        const int g = (co0 >> 2) + (gi >> 2) * 8 + 2 * (gi & 3) + h;
         const uint32_t off = ((uint32_t)(g * pps + slot) << 4) |
-                             ((uint32_t)(l32 >= G::MT * 4) << 31);
-        const float4 v = make_float4(my_sum, my_m2, cnt, 0.0f);
+                             ((uint32_t)((lane & 0x12) != 0) << 31);
+        const float4 v = make_float4(fmaf(K, cnt, S1),
+                                     fmaxf(S2 - S1 * S1 * inv_cnt, 0.0f), cnt, 0.0f);
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(u32x4, v), part_rsrc(n), off, 0, 0);
       }
@@ -828,39 +886,43 @@ __global__ void __launch_bounds__(G::NTHR)
       // (2) 4x4 window extrema.  The wave's 4 N-tiles are 4 consecutive
       // rows starting at a multiple of 4, and 4 consecutive lanes are 4
       // consecutive columns starting at a multiple of 4, so a window is
-      // (4 rows in-lane) x (4 lanes).  After the quad reduction all 4 lanes
-      // of a quad hold the window's value for every channel, so lane e of
-      // the quad stores channel 4-block element e.  Only the extremum that
-      // the monotone GroupNorm-affine-scale map sends to the window maximum
-      // is stored: the max where gamma*scale >= 0, else the min.
+      // (4 rows in-lane) x (4 lanes of a quad).  Only the extremum that the
+      // monotone GroupNorm-affine-scale map sends to the window maximum is
+      // stored: the max where gamma*scale >= 0, else the min.  Both are
+      // taken as a maximum of sg*y, sg = +-1 the channel's direction (exact:
+      // negation is exact and min(y) = -max(-y)), so each value enters one
+      // max chain.  Across the quad a halving exchange on lane bits 0 and 1
+      // leaves channel 2*b0 + b1 of the 4-channel block in each lane.
       const int py = (rt * G::TH + wm.row0) >> 2;
       const int px = (ct * G::TWC + wm.strip * 32 + l32) >> 2;
       const uint32_t win_off = (uint32_t)(py * a.Pw + px);
       const uint32_t win_bad = (uint32_t)!(py < a.Ph && px < a.Pw) << 31;
-      const int e = l32 & 3;
+      const bool q0 = lane & 1, q1 = (lane >> 1) & 1;
+      const int e = 2 * q0 + q1;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float mx[4], mn[4];
+          const int cq = co0 + mt * 32 + 8 * q + 4 * h;  // first channel
+          const f32x4 sg = *reinterpret_cast<const f32x4*>(&s_par[cq]);
+          f32x4 t;
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
-            const int i = 4 * q + e2;
-            float x = acc[mt][0][i], y = acc[mt][0][i];
+            float m = sg[e2] * acc[mt][0][4 * q + e2];
 #pragma unroll
-            for (int j = 1; j < G::NW; ++j) {
-              x = fmaxf(x, acc[mt][j][i]);
-              y = fminf(y, acc[mt][j][i]);
-            }
-            x = fmaxf(x, dpp<DPP_QUAD_XOR1>(x));
-            y = fminf(y, dpp<DPP_QUAD_XOR1>(y));
-            mx[e2] = fmaxf(x, dpp<DPP_QUAD_XOR2>(x));
-            mn[e2] = fminf(y, dpp<DPP_QUAD_XOR2>(y));
+            for (int j = 1; j < G::NW; ++j) m = vmax(m, sg[e2] * acc[mt][j][4 * q + e2]);
+            t[e2] = m;
           }
-          const float vmx = e == 0 ? mx[0] : (e == 1 ? mx[1] : (e == 2 ? mx[2] : mx[3]));
-          const float vmn = e == 0 ? mn[0] : (e == 1 ? mn[1] : (e == 2 ? mn[2] : mn[3]));
-          const int co = co0 + mt * 32 + 8 * q + 4 * h + e;
-          const float v = (s_par[co] != 0.0f) ? vmx : vmn;
+          f32x2 u = q0 ? t.hi : t.lo;
+          {
+            const f32x2 give = q0 ? t.lo : t.hi;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) u[k] = vmax(u[k], dpp<DPP_QUAD_XOR1>(give[k]));
+          }
+          const float r = vmax(q1 ? u.y : u.x, dpp<DPP_QUAD_XOR2>(q1 ? u.x : u.y));
+          const f32x2 s2 = q0 ? sg.hi : sg.lo;
+          const float v = (q1 ? s2.y : s2.x) * r;
+          const int co = cq + e;
           // NCHW: channel planes (padded channels fall past the end);
           // NHWC: channels innermost (padded channels get the drop bit)
           const uint32_t off =
