@@ -316,17 +316,28 @@ __global__ void __launch_bounds__(G::NTHR)
   const int nitems = my_tiles * a.ncb * a.nchunk;
 
   const uint32_t x_sample = (uint32_t)a.Cin * a.H * a.W;  // floats
-  const __amdgpu_buffer_rsrc_t w_rsrc =
-      make_rsrc(a.w, (uint32_t)a.Cout * a.Cin * 9u * 4u);
+  constexpr bool PRE = G::KO;  // precomputed staging offsets (see below)
+  const uint32_t w_total = (uint32_t)a.Cout * a.Cin * 9u;  // floats
 
   // ---- staging of one (tile, chunk) item ------------------------------------
   // The stage is filled in blocks, one direct-to-LDS load per block and
   // wave (lane l writes piece l of the block).  Wave w owns input blocks
   // w + NWAVE*i (i < NBI) and weight blocks w + NWAVE*i (i < NBW).
-  // Elements that must be zero (rows past H, input channels >= Cin, weight
-  // columns past the chunk's K) are read from an offset past the buffer end
-  // and land as 0; so do the weight rows of padded output channels, whose
-  // offsets lie past the end of the weight tensor by construction.
+  // PRE (the 16-byte NCHW configurations): a wave stages the same blocks
+  // of every item's tile, so the per-lane part of each block's source
+  // offset is computed once (xoff, woff); the item's position goes into the
+  // buffer resources, which are scalars, so the staging costs almost no
+  // vector instructions per item.  No input element is masked: rows past H
+  // and columns past W read the data that follows in the sample (values
+  // that reach only conv outputs outside the image, which are neither
+  // stored nor counted), and input channels past Cin start past the end of
+  // the sample and read as 0 -- as do the weight columns that meet them
+  // (past the chunk's K, masked).  The other configurations (4 times as
+  // many blocks, too many registers to keep) compute masked offsets per
+  // item: rows past H, input channels past Cin and weight columns past
+  // the chunk's K read as 0.  Either way the weight rows of padded output
+  // channels lie past the end of the weight tensor by construction and
+  // read as 0.
   //
   // Items run tile by tile; inside a tile, channel block by channel block;
   // inside a block, K chunk by K chunk.  A position in that walk is
@@ -361,11 +372,12 @@ __global__ void __launch_bounds__(G::NTHR)
   };
   // Uniform per-item limits, computed once per item.
   struct Lim {
-    __amdgpu_buffer_rsrc_t xr;
+    __amdgpu_buffer_rsrc_t xr;  // PRE: based at the item's first element
+    __amdgpu_buffer_rsrc_t wr;  // PRE: based at the item's first weight
     int base;      // element offset of (ci0, r0, c0) in the sample
-    int ci_lim;    // local channels < ci_lim are real (NHWC: and < CC)
-    int row_lim;   // local rows < row_lim are real
-    int col_lim;   // local columns < col_lim are needed and real
+    int ci_lim;    // masked staging (not PRE): local channels < ci_lim
+    int row_lim;   //   (NHWC: and < CC), rows < row_lim and columns <
+    int col_lim;   //   col_lim are real
     int kk_lim;    // weight columns < kk_lim are real
     int wbase;     // element offset of (co0, ci0) in the weight tensor
     int wslot;     // resident weights: the chunk's slot in ldsw
@@ -373,12 +385,17 @@ __global__ void __launch_bounds__(G::NTHR)
   const int HW = a.H * a.W, CinK = a.Cin * 9;
   auto lim_of = [&](const Item& it) X3_INLINE {
     Lim l;
-    l.xr = make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
     if constexpr (G::NHWC) {
+      l.xr = make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
       l.base = (it.r0 * a.W + it.c0) * a.Cin + it.ci0;
       const int cl = a.Cin - it.ci0;
       l.ci_lim = cl < G::CC ? cl : G::CC;
+    } else if constexpr (PRE) {
+      l.base = (it.ci0 * a.H + it.r0) * a.W + it.c0;
+      l.xr = make_rsrc(a.x + (size_t)it.n * x_sample + l.base,
+                       (x_sample - (uint32_t)l.base) * 4u);
     } else {
+      l.xr = make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
       l.base = (it.ci0 * a.H + it.r0) * a.W + it.c0;
       l.ci_lim = a.Cin - it.ci0;
     }
@@ -389,19 +406,57 @@ __global__ void __launch_bounds__(G::NTHR)
     const int kl = 9 * (a.Cin - it.ci0);
     l.kk_lim = kl < G::KC ? kl : G::KC;
     l.wbase = it.co0 * CinK + it.ci0 * 9;
+    l.wr = PRE ? make_rsrc(a.w + l.wbase, (w_total - (uint32_t)l.wbase) * 4u)
+               : make_rsrc(a.w, w_total * 4u);
     l.wslot = 0;
     return l;
   };
-  // Wave-local block i (compile-time) of the stage at `sbase`.  `zz` is an
-  // opaque per-item zero: it keeps the lane-dependent address arithmetic
-  // from being hoisted out of the item loop (which would pin one register
-  // per block for the whole kernel).
+  // Per-lane staging offsets (bytes) of the wave's input and weight
+  // blocks; bit 31 set = never loaded (stage padding past CC channels,
+  // weight-row padding past K).
+  uint32_t xoff[PRE ? G::NBI : 1];
+  uint32_t woff[PRE ? G::NBW : 1], wkk[PRE ? G::NBW : 1];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int i = 0; i < G::NBI; ++i) {
+      int blk = wave + i * G::NWAVE;
+      blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
+      // first dword of this lane's piece; with X4 the lane moves 4
+      // consecutive dwords of one row (XP and CS are multiples of 4, so a
+      // piece never crosses a row)
+      const uint32_t p = (uint32_t)(blk * G::XBLK + lane * (G::XBLK / 64));
+      const uint32_t cil = p / G::CS;
+      const uint32_t rem = p - cil * G::CS;
+      const uint32_t row = rem / G::XP;
+      const uint32_t col = rem - row * G::XP;
+      xoff[i] = ((cil * (uint32_t)HW + row * (uint32_t)a.W + col) << 2) |
+                ((uint32_t)(cil >= (uint32_t)G::CC) << 31);
+    }
+#pragma unroll
+    for (int i = 0; i < G::NBW; ++i) {
+      int blk = wave + i * G::NWAVE;
+      blk = blk < G::NBWT - 1 ? blk : G::NBWT - 1;
+      // lane l moves 4 consecutive floats of one weight row (the pitch
+      // and the row's K columns are multiples of 4; the dispatch keeps
+      // Cin % 4 == 0 so the global rows are 16-byte aligned too)
+      const uint32_t q = (uint32_t)(blk * G::WBLK + lane * (G::WBLK / 64));
+      const uint32_t co = q / G::WP;
+      const uint32_t kk = q - co * G::WP;
+      wkk[i] = kk;
+      woff[i] = ((co * (uint32_t)CinK + kk) << 2) |
+                ((uint32_t)(kk >= (uint32_t)G::KC) << 31);
+    }
+  }
+  // Wave-local block i (compile-time) of the stage at `sbase`.  An element
+  // that must read as zero gets bit 31 set in its offset: every buffer here
+  // is smaller than 2 GiB, so such an offset is past num_records and the
+  // load returns 0.  (An OR rather than a select keeps the compiler from
+  // turning this into an exec-masked region.)  Without PRE the offsets are
+  // computed per item, masked; `zz` is an opaque per-item zero that keeps
+  // that lane-dependent arithmetic from being hoisted out of the item loop
+  // (which would pin one register per block for the whole kernel).
   auto issue = [&](const Lim& l, X3_LDS float* sbase, int i, int zz)
                    X3_INLINE {
-    // An element that must read as zero gets bit 31 set in its offset:
-    // every buffer here is smaller than 2 GiB, so such an offset is past
-    // num_records and the load returns 0.  (An OR rather than a select
-    // keeps the compiler from turning this into an exec-masked region.)
     if (i < G::NBI && G::NHWC) {
       int blk = wave + zz + i * G::NWAVE;
       blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
@@ -421,56 +476,52 @@ __global__ void __launch_bounds__(G::NTHR)
             (uint32_t)l.base) << 2) | ((uint32_t)!ok << 31);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           l.xr, (X3_LDS void*)(sbase + blk * 64), 4, off, 0, 0, 0);
+    } else if (i < G::NBI && PRE) {
+      int blk = wave + i * G::NWAVE;
+      blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
+      lds_load_x4(l.xr, (X3_LDS void*)(sbase + blk * G::XBLK), xoff[i]);
     } else if (i < G::NBI) {
       int blk = wave + zz + i * G::NWAVE;
       blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
-      // first dword of this lane's piece; with X4 the lane moves 4
-      // consecutive dwords of one row (XP and CS are multiples of 4, so a
-      // piece never crosses a row).  A piece whose first element is needed
-      // is loaded whole: its other elements are either needed too or lie in
-      // columns >= W - c0, which only feed masked output columns.
       const uint32_t p = (uint32_t)(blk * G::XBLK + lane * (G::XBLK / 64));
       const uint32_t cil = p / G::CS;
       const uint32_t rem = p - cil * G::CS;
       const uint32_t row = rem / G::XP;
       const uint32_t col = rem - row * G::XP;
-      // (KO rounds the stage up to whole blocks: slots past CC channels
-      // are padding)
       const bool ok = (cil < (uint32_t)l.ci_lim) &
-                      (!G::KO || cil < (uint32_t)G::CC) &
                       (row < (uint32_t)l.row_lim) &
                       (col < (uint32_t)l.col_lim);
       const uint32_t off =
           ((cil * (uint32_t)HW + row * (uint32_t)a.W + col +
             (uint32_t)l.base) << 2) | ((uint32_t)!ok << 31);
-      X3_LDS void* dst = (X3_LDS void*)(sbase + blk * G::XBLK);
-      if constexpr (G::X4)
-        lds_load_x4(l.xr, dst, off);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(l.xr, dst, 4, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          l.xr, (X3_LDS void*)(sbase + blk * G::XBLK), 4, off, 0, 0, 0);
     } else {
-      int blk = wave + zz + (i - G::NBI) * G::NWAVE;
+      const int iw = i - G::NBI;
+      int blk = wave + (PRE ? 0 : zz) + iw * G::NWAVE;
       blk = blk < G::NBWT - 1 ? blk : G::NBWT - 1;
-      // KO: lane l moves 4 consecutive floats of one weight row (the pitch
-      // and the row's K columns are multiples of 4; the dispatch keeps
-      // Cin % 4 == 0 so the global rows are 16-byte aligned too).  Columns
-      // past the chunk's K (and the row padding) read as zero.
-      const uint32_t q = (uint32_t)(blk * G::WBLK + lane * (G::WBLK / 64));
-      const uint32_t co = q / G::WP;
-      const uint32_t kk = q - co * G::WP;
-      const bool ok = kk < (uint32_t)l.kk_lim;
-      const uint32_t off =
-          ((co * (uint32_t)CinK + (uint32_t)l.wbase + kk) << 2) |
-          ((uint32_t)!ok << 31);
       X3_LDS float* wdst =
           G::RESW ? (X3_LDS float*)ldsw + l.wslot * G::WBUF : sbase + G::XBUF;
       X3_LDS void* dst = (X3_LDS void*)(wdst + blk * G::WBLK);
-      if constexpr (G::KO)
-        lds_load_x4(w_rsrc, dst, off);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, dst, 4, off, 0, 0, 0);
+      if constexpr (PRE) {
+        // columns past the chunk's K (a last chunk of fewer than CC
+        // channels) read as zero
+        const uint32_t off =
+            woff[iw] | ((uint32_t)(wkk[iw] >= (uint32_t)l.kk_lim) << 31);
+        lds_load_x4(l.wr, dst, off);
+      } else {
+        const uint32_t q = (uint32_t)(blk * G::WBLK + lane);
+        const uint32_t co = q / G::WP;
+        const uint32_t kk = q - co * G::WP;
+        const bool ok = kk < (uint32_t)l.kk_lim;
+        const uint32_t off =
+            ((co * (uint32_t)CinK + (uint32_t)l.wbase + kk) << 2) |
+            ((uint32_t)!ok << 31);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(l.wr, dst, 4, off, 0, 0, 0);
+      }
     }
   };
+
   // blocks per wave per item, BPS per k-step over the first half of the
   // k-steps, so that they have the second half to land
   constexpr int NB_W = G::NB_ITEM;
@@ -1073,6 +1124,8 @@ __global__ void __launch_bounds__(G::NTHR)
         if (c < a.nchunk) {
           Lim lc = l0;
           lc.wbase = c * G::CC * 9;
+          if constexpr (PRE)
+            lc.wr = make_rsrc(a.w + lc.wbase, (w_total - (uint32_t)lc.wbase) * 4u);
           const int kl = 9 * (a.Cin - c * G::CC);
           lc.kk_lim = kl < G::KC ? kl : G::KC;
           lc.wslot = c;
