@@ -122,3 +122,34 @@ def test_nhwc_matches_nchw_on_full_width_shape():
     n = {k: v.numpy() for k, v in d.items()}
     close(b, oracle.mul_lrelu_gelu(n["x"], n["weight"], n["bias"], n["multiplier"], 0.01),
           "gelu 258")
+
+
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+def test_nonfinite_input_stays_local(layout):
+    """An infinite input element reaches only the outputs whose 3x3 window
+    contains it.  Cin = 12 leaves the last K chunk with 4 real channels, so
+    the staging must read the missing ones as zeros rather than as the
+    following data (the next pixel in NHWC, the next sample in NCHW)."""
+    B, Cin, H, W, Cout = 2, 12, 20, 67, 64
+    d = random_case("mul_lrelu_gelu", B, Cin, H, W, Cout, seed=1950)
+    hits = [(1, 5, 0), (0, 7, 0), (1, 0, 0)]  # (n, row, col): channels 0-3 infinite
+    for n, r, c in hits:
+        d["x"][n, 0:4, r, c] = float("inf")
+    g = dev_cl(d) if layout == "nhwc" else {k: v.to(DEV) for k, v in d.items()}
+    Ho, Wo = H - 2, W - 2
+    clean = np.ones((B, Ho, Wo), dtype=bool)
+    for n, r, c in hits:
+        clean[n, max(r - 2, 0):r + 1, max(c - 2, 0):c + 1] = False
+    n_ = {k: v.numpy() for k, v in d.items()}
+    for name, got, ref in [
+        ("min_tanh2", x3.conv3x3_min_tanh2(g["x"], g["weight"], g["bias"]),
+         oracle.min_tanh2(n_["x"], n_["weight"], n_["bias"])),
+        ("gelu", x3.conv3x3_mul_lrelu_gelu(g["x"], g["weight"], g["bias"], g["multiplier"]),
+         oracle.mul_lrelu_gelu(n_["x"], n_["weight"], n_["bias"], n_["multiplier"], 0.01)),
+    ]:
+        got = got.detach().cpu().numpy().astype(np.float64)
+        m = np.broadcast_to(clean[:, None], got.shape)
+        assert np.all(np.isfinite(got[m])), name
+        err = float(np.abs(got[m] - ref[m]).max())
+        say(f"  {layout} {name}: max_abs_err on clean outputs={err:.3e}")
+        assert err <= TOL, (name, err)

@@ -121,11 +121,19 @@ struct Geo {
   // stage the input only.
   static constexpr int RC = RC_;
   static constexpr bool RESW = RC > 0;
-  // x (and the per-channel outputs) in NHWC order: the input tile is staged
-  // pixel-major, [XROWS][XCOLS][CCP], CCP = CC + 2.  With a pitch of 2 mod 4
-  // dwords per pixel, the 32 pixels x 2 adjacent channels of a B-fragment
-  // read (lane half h reads channel 2cp + h) fall in 64 distinct banks.
+  // x (and the per-channel outputs) in NHWC order.
+  //  * 4-byte staging: the input tile is staged pixel-major,
+  //    [XROWS][XCOLS][CCP], CCP = CC + 2.  With a pitch of 2 mod 4 dwords
+  //    per pixel, the 32 pixels x 2 adjacent channels of a B-fragment read
+  //    (lane half h reads channel 2cp + h) fall in 64 distinct banks.
+  //  * NH4, 16-byte staging (Cin % 4 == 0): two regions, channels 0-3 and
+  //    4-7 of the chunk, each [XROWS][XCOLS][4], so a 16-byte piece is one
+  //    pixel's 4 channels.  K order: k-step s takes tap s/4, and lane half
+  //    h channel 4h + s%4, so a lane's B values of the 4 k-steps of a tap
+  //    are one ds_read_b128; 16 consecutive pixels at a 4-dword pitch cover
+  //    all 64 banks.
   static constexpr bool NHWC = NHWC_;
+  static constexpr bool NH4 = NHWC_ && X4_;
   static constexpr int CCP = CC + 2;
   static constexpr int NTHR = NWAVE * 64;
   static constexpr int COUT = 32 * MT;    // channels per pass
@@ -147,6 +155,7 @@ struct Geo {
   //    adjacent channels), odd weight pitch WP = KC + 1 (conflict-free
   //    4-byte reads).
   static constexpr bool KO = X4 && !NHWC;
+  static constexpr int RSZ = (XROWS * XCOLS * 4 + 255) / 256 * 256;  // NH4 region
   static constexpr int CS0 = XROWS * XP;
   static constexpr int CS =
       KO ? CS0 + ((8 - (CS0 % 16)) + 16) % 16
@@ -154,16 +163,18 @@ struct Geo {
   static constexpr int KC = 9 * CC;       // K per chunk
   static constexpr int XBLK = X4 ? 256 : 64;
   static constexpr int XBUF =             // input dwords per stage
-      NHWC ? (XROWS * XCOLS * CCP + 63) / 64 * 64
-           : (CC * CS + XBLK - 1) / XBLK * XBLK;
-  static constexpr int WP = KO ? KC + 4 : KC + 1;  // weight-row pitch
+      NH4    ? 2 * RSZ
+      : NHWC ? (XROWS * XCOLS * CCP + 63) / 64 * 64
+             : (CC * CS + XBLK - 1) / XBLK * XBLK;
+  // weight-row pitch: 16-byte staged rows (KO and NH4) as described for KO
+  static constexpr int WP = X4 ? KC + 4 : KC + 1;
   static constexpr int WBUF = COUT * WP;  // weight dwords per stage
   // Staging blocks: the input region is filled in blocks of 256 dwords
   // (16 bytes per lane, X4) or 64 dwords (4 bytes per lane), the weight
   // region likewise (256 with KO).  Every wavefront issues the same number
   // of blocks, NBI + NBW per item; a wavefront whose turn runs past the
   // last block reloads the last block (same data to the same place).
-  static constexpr int WBLK = KO ? 256 : 64;
+  static constexpr int WBLK = X4 ? 256 : 64;
   static constexpr int NBX = XBUF / XBLK;                 // input blocks
   static constexpr int NBWT = WBUF / WBLK;                // weight blocks
   static constexpr int NBI = (NBX + NWAVE - 1) / NWAVE;   // per wave
@@ -177,8 +188,8 @@ struct Geo {
   static constexpr int NW = NTILE_N / NWAVE;  // N-tiles per wave
 
   static_assert(CC % 2 == 0, "CC must be even");
-  static_assert(!NHWC || (CC % 4 == 0 && !X4),
-                "NHWC: CC % 4 == 0 (pitch 2 mod 4), 4-byte staging");
+  static_assert(!NHWC || CC % 4 == 0, "NHWC: CC % 4 == 0 (pitch 2 mod 4)");
+  static_assert(!NH4 || (CC == 8 && KS % 4 == 0), "NH4: 8-channel chunks");
   static_assert(XBUF % XBLK == 0 && WBUF % WBLK == 0, "whole staging blocks");
   static_assert(!KO || (CC == 8 && KS % 4 == 0 && (CC / 2 * CS) % 64 == 32),
                 "KO: 8-channel chunks, halves in opposite bank halves");
@@ -316,28 +327,31 @@ __global__ void __launch_bounds__(G::NTHR)
   const int nitems = my_tiles * a.ncb * a.nchunk;
 
   const uint32_t x_sample = (uint32_t)a.Cin * a.H * a.W;  // floats
-  constexpr bool PRE = G::KO;  // precomputed staging offsets (see below)
+  constexpr bool PRE = G::X4;  // precomputed staging offsets (see below)
   const uint32_t w_total = (uint32_t)a.Cout * a.Cin * 9u;  // floats
+  // a buffer of no records: every load through it returns 0
+  const __amdgpu_buffer_rsrc_t x_null = make_rsrc(a.x, 0u);
 
   // ---- staging of one (tile, chunk) item ------------------------------------
   // The stage is filled in blocks, one direct-to-LDS load per block and
   // wave (lane l writes piece l of the block).  Wave w owns input blocks
   // w + NWAVE*i (i < NBI) and weight blocks w + NWAVE*i (i < NBW).
-  // PRE (the 16-byte NCHW configurations): a wave stages the same blocks
-  // of every item's tile, so the per-lane part of each block's source
-  // offset is computed once (xoff, woff); the item's position goes into the
-  // buffer resources, which are scalars, so the staging costs almost no
-  // vector instructions per item.  No input element is masked: rows past H
-  // and columns past W read the data that follows in the sample (values
+  // PRE (the 16-byte configurations, NCHW and NHWC): a wave stages the same
+  // blocks of every item's tile, so the per-lane part of each block's
+  // source offset is computed once (xoff, woff); the item's position goes
+  // into the buffer resources, which are scalars, so the staging costs
+  // almost no vector instructions per item.  Rows past H and columns past W
+  // are not masked: they read the data that follows in the sample (values
   // that reach only conv outputs outside the image, which are neither
-  // stored nor counted), and input channels past Cin start past the end of
-  // the sample and read as 0 -- as do the weight columns that meet them
-  // (past the chunk's K, masked).  The other configurations (4 times as
-  // many blocks, too many registers to keep) compute masked offsets per
-  // item: rows past H, input channels past Cin and weight columns past
-  // the chunk's K read as 0.  Either way the weight rows of padded output
-  // channels lie past the end of the weight tensor by construction and
-  // read as 0.
+  // stored nor counted) or lie past its end and read as 0.  Input channels
+  // past Cin read as 0 too: in NCHW they start past the end of the sample;
+  // in NHWC (Cin % 8 == 4: the upper half of a last chunk) their blocks
+  // load through a buffer of no records.  Weight columns past the chunk's
+  // K are masked.  The other configurations (4 times as many blocks, too
+  // many registers to keep) compute masked offsets per item: rows past H,
+  // input channels past Cin and weight columns past the chunk's K read as
+  // 0.  Either way the weight rows of padded output channels lie past the
+  // end of the weight tensor by construction and read as 0.
   //
   // Items run tile by tile; inside a tile, channel block by channel block;
   // inside a block, K chunk by K chunk.  A position in that walk is
@@ -385,7 +399,12 @@ __global__ void __launch_bounds__(G::NTHR)
   const int HW = a.H * a.W, CinK = a.Cin * 9;
   auto lim_of = [&](const Item& it) X3_INLINE {
     Lim l;
-    if constexpr (G::NHWC) {
+    if constexpr (G::NH4) {
+      l.base = (it.r0 * a.W + it.c0) * a.Cin + it.ci0;
+      l.xr = make_rsrc(a.x + (size_t)it.n * x_sample + l.base,
+                       (x_sample - (uint32_t)l.base) * 4u);
+      l.ci_lim = a.Cin - it.ci0;
+    } else if constexpr (G::NHWC) {
       l.xr = make_rsrc(a.x + (size_t)it.n * x_sample, x_sample * 4u);
       l.base = (it.r0 * a.W + it.c0) * a.Cin + it.ci0;
       const int cl = a.Cin - it.ci0;
@@ -416,7 +435,22 @@ __global__ void __launch_bounds__(G::NTHR)
   // weight-row padding past K).
   uint32_t xoff[PRE ? G::NBI : 1];
   uint32_t woff[PRE ? G::NBW : 1], wkk[PRE ? G::NBW : 1];
-  if constexpr (PRE) {
+  constexpr int RBLK = G::RSZ / 256;  // NH4: blocks per channel-half region
+  if constexpr (G::NH4) {
+#pragma unroll
+    for (int i = 0; i < G::NBI; ++i) {
+      int blk = wave + i * G::NWAVE;
+      blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
+      // lane l moves pixel pc's 4 channels of the block's half; pieces
+      // past the tile's pixels (region padding) are not loaded
+      const int hr = blk >= RBLK;
+      const uint32_t pc = (uint32_t)((blk - hr * RBLK) * 64 + lane);
+      const uint32_t row = pc / G::XCOLS;
+      const uint32_t col = pc - row * G::XCOLS;
+      xoff[i] = (((row * (uint32_t)a.W + col) * (uint32_t)a.Cin + 4u * hr) << 2) |
+                ((uint32_t)(pc >= (uint32_t)(G::XROWS * G::XCOLS)) << 31);
+    }
+  } else if constexpr (PRE) {
 #pragma unroll
     for (int i = 0; i < G::NBI; ++i) {
       int blk = wave + i * G::NWAVE;
@@ -432,6 +466,8 @@ __global__ void __launch_bounds__(G::NTHR)
       xoff[i] = ((cil * (uint32_t)HW + row * (uint32_t)a.W + col) << 2) |
                 ((uint32_t)(cil >= (uint32_t)G::CC) << 31);
     }
+  }
+  if constexpr (PRE) {
 #pragma unroll
     for (int i = 0; i < G::NBW; ++i) {
       int blk = wave + i * G::NWAVE;
@@ -457,7 +493,13 @@ __global__ void __launch_bounds__(G::NTHR)
   // (which would pin one register per block for the whole kernel).
   auto issue = [&](const Lim& l, X3_LDS float* sbase, int i, int zz)
                    X3_INLINE {
-    if (i < G::NBI && G::NHWC) {
+    if (i < G::NBI && G::NH4) {
+      int blk = wave + i * G::NWAVE;
+      blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
+      // (uniform) the upper channel half of a last chunk with 4 channels
+      const bool none = blk >= RBLK && l.ci_lim <= 4;
+      lds_load_x4(none ? x_null : l.xr, (X3_LDS void*)(sbase + blk * 256), xoff[i]);
+    } else if (i < G::NBI && G::NHWC) {
       int blk = wave + zz + i * G::NWAVE;
       blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
       // LDS dword p of the tile is (pixel p / CCP, channel slot p % CCP);
@@ -1024,20 +1066,32 @@ __global__ void __launch_bounds__(G::NTHR)
     }
 
     const X3_LDS float* xs =
-        G::NHWC ? cur + (wm.row0 * G::XCOLS + wm.strip * 32 + l32) * G::CCP + h
-        : G::KO ? cur + h * (G::CC / 2) * G::CS + wm.row0 * G::XP +
-                      wm.strip * 32 + l32
-                : cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
+        G::NH4    ? cur + h * G::RSZ + (wm.row0 * G::XCOLS + wm.strip * 32 + l32) * 4
+        : G::NHWC ? cur + (wm.row0 * G::XCOLS + wm.strip * 32 + l32) * G::CCP + h
+        : G::KO   ? cur + h * (G::CC / 2) * G::CS + wm.row0 * G::XP +
+                        wm.strip * 32 + l32
+                  : cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
+    // (a weight row holds K index ci*9 + tap; lane half h starts at channel
+    // CC/2 * h for KO and NH4, which is K index 36h = KS*h)
     const X3_LDS float* ws =
         (G::RESW ? (const X3_LDS float*)ldsw + chunk * G::WBUF
-                 : cur + G::XBUF) + l32 * G::WP + h * (G::KO ? G::KS : 9);
+                 : cur + G::XBUF) + l32 * G::WP + h * (G::X4 ? G::KS : 9);
     // Software pipeline over the k-steps of the chunk: step s issues the LDS
     // fragment reads of step s+1, its share of the next item's staging
     // loads, then its MFMAs; a scheduling fence keeps that order, so each
     // MFMA's operands were requested a full step (MT*NW MFMAs) earlier.
-    // KO reads the weights of 4 k-steps at once, a group ahead.
+    // KO reads the weights of 4 k-steps at once, a group ahead; NH4 reads
+    // the input values of the 4 k-steps of a tap at once, a tap ahead.
     float av[2][G::MT], bv[2][G::NW];
     f32x4 a4[2][G::KO ? G::MT : 1];
+    f32x4 b4[2][G::NH4 ? G::NW : 1];
+    auto load_b4 = [&](int tap, f32x4 (&Bq)[G::NH4 ? G::NW : 1]) X3_INLINE {
+      const int kh = tap / 3, kw = tap % 3;
+#pragma unroll
+      for (int j = 0; j < (G::NH4 ? G::NW : 1); ++j)
+        Bq[j] = *reinterpret_cast<const X3_LDS f32x4*>(
+            xs + ((j + kh) * G::XCOLS + kw) * 4);
+    };
     auto load_a4 = [&](int g, f32x4 (&A)[G::KO ? G::MT : 1]) X3_INLINE {
 #pragma unroll
       for (int mt = 0; mt < (G::KO ? G::MT : 1); ++mt)
@@ -1045,7 +1099,14 @@ __global__ void __launch_bounds__(G::NTHR)
                                                        4 * g);
     };
     auto load_frag = [&](int s, float (&A)[G::MT], float (&Bv)[G::NW]) X3_INLINE {
-      if constexpr (G::KO) {
+      if constexpr (G::NH4) {
+        // k-step s: tap s/4, channel 4h + s%4 (K index (4h + s%4)*9 + tap)
+        const int tap = s / 4, cq = s % 4;
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt)
+          A[mt] = ws[mt * 32 * G::WP + cq * 9 + tap];
+        (void)Bv;
+      } else if constexpr (G::KO) {
         const int ci = s / 9, tap = s % 9, kh = tap / 3, kw = tap % 3;
 #pragma unroll
         for (int j = 0; j < G::NW; ++j)
@@ -1064,12 +1125,17 @@ __global__ void __launch_bounds__(G::NTHR)
       }
     };
     if constexpr (G::KO) load_a4(0, a4[0]);
+    if constexpr (G::NH4) load_b4(0, b4[0]);
     load_frag(0, av[0], bv[0]);
 #pragma unroll
     for (int s = 0; s < G::KS; ++s) {
       if constexpr (G::KO) {
         if (s % 4 == 0 && s / 4 + 1 < G::KS / 4)
           load_a4(s / 4 + 1, a4[(s / 4 + 1) & 1]);
+      }
+      if constexpr (G::NH4) {
+        if (s % 4 == 0 && s / 4 + 1 < G::KS / 4)
+          load_b4(s / 4 + 1, b4[(s / 4 + 1) & 1]);
       }
       if (s + 1 < G::KS) load_frag(s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
       // (unconditional: on the last item this reloads the current item's
@@ -1088,7 +1154,8 @@ __global__ void __launch_bounds__(G::NTHR)
         for (int j = 0; j < G::NW; ++j)
           acc[mt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
               G::KO ? a4[(s / 4) & 1][mt][s % 4] : av[s & 1][mt],
-              bv[s & 1][j], acc[mt][j], 0, 0, 0);
+              G::NH4 ? b4[(s / 4) & 1][G::NH4 ? j : 0][s % 4] : bv[s & 1][j],
+              acc[mt][j], 0, 0, 0);
       // Issue order inside the step: each MFMA (64 cycles in the matrix
       // core) is followed by a slice of this wave's other work -- LDS
       // fragment reads, staging address arithmetic, one staging load -- so

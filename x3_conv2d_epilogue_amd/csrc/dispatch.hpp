@@ -40,6 +40,13 @@ inline bool rows_aligned16(const x3::ConvArgs& a) {
          (((uintptr_t)a.w & 15u) == 0);
 }
 
+// NHWC x takes 16-byte staging when a pixel's channels start 16-byte
+// aligned (Cin % 4 == 0, x aligned) and the weight rows do too.
+inline bool nhwc_aligned16(const x3::ConvArgs& a) {
+  return (a.Cin % 4 == 0) && (((uintptr_t)a.x & 15u) == 0) &&
+         (((uintptr_t)a.w & 15u) == 0);
+}
+
 template <class G, int EPI>
 x3_status run_conv(x3::ConvArgs a, hipStream_t st) {
   a.n_rt = (a.Ho + G::TH - 1) / G::TH;
@@ -79,50 +86,56 @@ x3_status run_conv(x3::ConvArgs a, hipStream_t st) {
 // MFMA blocks).  The tile width follows the output width.
 
 // 64-channel blocks: 2 channel blocks x 4 N-tiles per wave, TH*NCT = 32.
-template <int EPI, bool X4>
+// (NH: NHWC x, 16-byte staging -- X4 must be set too)
+template <int EPI, bool X4, bool NH = false>
 x3_status dispatch_mt2(const x3::ConvArgs& a, hipStream_t st) {
-  if (a.Wo > 128) return run_conv<x3::Geo<2, 8, 4, 8, 8, X4>, EPI>(a, st);
-  if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8, X4>, EPI>(a, st);
-  if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8, X4>, EPI>(a, st);
-  return run_conv<x3::Geo<2, 8, 32, 1, 8, X4>, EPI>(a, st);
+  if (a.Wo > 128) return run_conv<x3::Geo<2, 8, 4, 8, 8, X4, 0, NH>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8, X4, 0, NH>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8, X4, 0, NH>, EPI>(a, st);
+  return run_conv<x3::Geo<2, 8, 32, 1, 8, X4, 0, NH>, EPI>(a, st);
 }
 
 // 128-channel blocks: 4 channel blocks x 2 N-tiles per wave, TH*NCT = 16.
-template <int EPI, bool X4>
+template <int EPI, bool X4, bool NH = false>
 x3_status dispatch_mt4(const x3::ConvArgs& a, hipStream_t st) {
-  if (a.Wo > 128) return run_conv<x3::Geo<4, 8, 2, 8, 8, X4>, EPI>(a, st);
-  if (a.Wo > 64) return run_conv<x3::Geo<4, 8, 4, 4, 8, X4>, EPI>(a, st);
-  if (a.Wo > 32) return run_conv<x3::Geo<4, 8, 8, 2, 8, X4>, EPI>(a, st);
-  return run_conv<x3::Geo<4, 8, 16, 1, 8, X4>, EPI>(a, st);
+  if (a.Wo > 128) return run_conv<x3::Geo<4, 8, 2, 8, 8, X4, 0, NH>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<4, 8, 4, 4, 8, X4, 0, NH>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<4, 8, 8, 2, 8, X4, 0, NH>, EPI>(a, st);
+  return run_conv<x3::Geo<4, 8, 16, 1, 8, X4, 0, NH>, EPI>(a, st);
 }
 
 // The same tiles with the weights of (up to) two K chunks resident in LDS:
 // Cin <= 16 and one channel block (Cout <= 64 or 128).  16-byte staging only.
-template <int EPI>
+template <int EPI, bool NH = false>
 x3_status dispatch_mt2_rw(const x3::ConvArgs& a, hipStream_t st) {
-  if (a.Wo > 128) return run_conv<x3::Geo<2, 8, 4, 8, 8, true, 2>, EPI>(a, st);
-  if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8, true, 2>, EPI>(a, st);
-  if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8, true, 2>, EPI>(a, st);
-  return run_conv<x3::Geo<2, 8, 32, 1, 8, true, 2>, EPI>(a, st);
+  if (a.Wo > 128) return run_conv<x3::Geo<2, 8, 4, 8, 8, true, 2, NH>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8, true, 2, NH>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8, true, 2, NH>, EPI>(a, st);
+  return run_conv<x3::Geo<2, 8, 32, 1, 8, true, 2, NH>, EPI>(a, st);
 }
-template <int EPI>
+template <int EPI, bool NH = false>
 x3_status dispatch_mt4_rw(const x3::ConvArgs& a, hipStream_t st) {
-  if (a.Wo > 128) return run_conv<x3::Geo<4, 8, 2, 8, 8, true, 2>, EPI>(a, st);
-  if (a.Wo > 64) return run_conv<x3::Geo<4, 8, 4, 4, 8, true, 2>, EPI>(a, st);
-  if (a.Wo > 32) return run_conv<x3::Geo<4, 8, 8, 2, 8, true, 2>, EPI>(a, st);
-  return run_conv<x3::Geo<4, 8, 16, 1, 8, true, 2>, EPI>(a, st);
+  if (a.Wo > 128) return run_conv<x3::Geo<4, 8, 2, 8, 8, true, 2, NH>, EPI>(a, st);
+  if (a.Wo > 64) return run_conv<x3::Geo<4, 8, 4, 4, 8, true, 2, NH>, EPI>(a, st);
+  if (a.Wo > 32) return run_conv<x3::Geo<4, 8, 8, 2, 8, true, 2, NH>, EPI>(a, st);
+  return run_conv<x3::Geo<4, 8, 16, 1, 8, true, 2, NH>, EPI>(a, st);
+}
+
+// The 16-byte configurations (NCHW, or NHWC with NH), resident weights
+// when they fit: all K chunks of the one channel block.
+template <int EPI, bool NH>
+x3_status dispatch_x4(const x3::ConvArgs& a, hipStream_t st) {
+  const int mt = channel_block_mt(a.Cout);
+  if (a.Cin <= 16 && a.Cout <= 32 * mt)
+    return mt == 4 ? dispatch_mt4_rw<EPI, NH>(a, st) : dispatch_mt2_rw<EPI, NH>(a, st);
+  return mt == 4 ? dispatch_mt4<EPI, true, NH>(a, st) : dispatch_mt2<EPI, true, NH>(a, st);
 }
 
 template <int EPI>
 x3_status dispatch(const x3::ConvArgs& a, hipStream_t st) {
-  const bool x4 = rows_aligned16(a);
-  const int mt = channel_block_mt(a.Cout);
-  // resident weights when they fit: all K chunks of the one channel block
-  if (x4 && a.Cin <= 16 && a.Cout <= 32 * mt)
-    return mt == 4 ? dispatch_mt4_rw<EPI>(a, st) : dispatch_mt2_rw<EPI>(a, st);
-  if (mt == 4)
-    return x4 ? dispatch_mt4<EPI, true>(a, st) : dispatch_mt4<EPI, false>(a, st);
-  return x4 ? dispatch_mt2<EPI, true>(a, st) : dispatch_mt2<EPI, false>(a, st);
+  if (rows_aligned16(a)) return dispatch_x4<EPI, false>(a, st);
+  if (channel_block_mt(a.Cout) == 4) return dispatch_mt4<EPI, false>(a, st);
+  return dispatch_mt2<EPI, false>(a, st);
 }
 
 // Per-epilogue launchers, one translation unit each.

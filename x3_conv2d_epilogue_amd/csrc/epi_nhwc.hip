@@ -1,9 +1,12 @@
 // epi_nhwc.hip -- the fused kernels for NHWC (channels-last) x, and the
-// NHWC GroupNorm finalize.  The input tile is staged pixel-major with a
-// 10-dword pixel pitch (8 channels + 2 padding) and 4-byte direct-to-LDS
-// loads; the MFMA loop and the epilogues are those of the NCHW kernels.
-// Tiles are at most 128 columns wide: the pixel-major tile is 1.25x the
-// size of the channel-major one.
+// NHWC GroupNorm finalize.  With Cin % 4 == 0 (and 16-byte aligned x and
+// w) the input tile is staged with 16-byte direct-to-LDS loads in two
+// channel-half regions (4 channels per pixel each) and the kernels take
+// the tiles of the NCHW ones; otherwise it is staged pixel-major with a
+// 10-dword pixel pitch (8 channels + 2 padding) and 4-byte loads, in tiles
+// of at most 128 columns (the pixel-major tile is 1.25x the size of the
+// channel-major one).  The MFMA loop and the epilogues are those of the
+// NCHW kernels.
 #include "dispatch.hpp"
 
 namespace x3i {
@@ -27,6 +30,7 @@ x3_status dispatch_nhwc_mt2(const x3::ConvArgs& a, hipStream_t st) {
 
 template <int EPI>
 x3_status dispatch_nhwc(const x3::ConvArgs& a, hipStream_t st) {
+  if (nhwc_aligned16(a)) return dispatch_x4<EPI, true>(a, st);
   if (channel_block_mt(a.Cout) == 4) {
     if (a.Wo > 64) return run_conv<GeoN<4, 4, 4>, EPI>(a, st);
     if (a.Wo > 32) return run_conv<GeoN<4, 8, 2>, EPI>(a, st);
@@ -35,8 +39,19 @@ x3_status dispatch_nhwc(const x3::ConvArgs& a, hipStream_t st) {
   return dispatch_nhwc_mt2<EPI>(a, st);
 }
 
+// (the 16-byte configurations take the same tile shapes as the 4-byte
+// ones, so the GroupNorm partial slots do not depend on the alignment)
 template <int EPI>
 x3_status dispatch_gn_nhwc(const x3::ConvArgs& a, hipStream_t st) {
+  if (nhwc_aligned16(a)) {
+    if (gn_resident_nhwc(a.Cin, a.Cout)) {
+      if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 8, 2, 4, true, 1, true>, EPI>(a, st);
+      return run_conv<x3::Geo<2, 8, 16, 1, 4, true, 1, true>, EPI>(a, st);
+    }
+    if (a.Wo > 64) return run_conv<x3::Geo<2, 8, 8, 4, 8, true, 0, true>, EPI>(a, st);
+    if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 16, 2, 8, true, 0, true>, EPI>(a, st);
+    return run_conv<x3::Geo<2, 8, 32, 1, 8, true, 0, true>, EPI>(a, st);
+  }
   if (gn_resident_nhwc(a.Cin, a.Cout)) {
     if (a.Wo > 32) return run_conv<GeoNR<8, 2>, EPI>(a, st);
     return run_conv<GeoNR<16, 1>, EPI>(a, st);
