@@ -244,7 +244,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-others", action="store_true",
-                    help="do not time the other four workloads")
+                    help="do not time the other four workloads (the unfused and NHWC "
+                         "comparisons then cover the chosen workload only)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the unfused (conv + standalone epilogue) comparison")
     ap.add_argument("--no-nhwc", action="store_true",
@@ -357,7 +358,7 @@ def main():
     if not args.no_nhwc:
         for name in WORKLOAD_ORDER:
             w2 = WORKLOADS[name]
-            if w2.B * w2.Cout < 1024:
+            if w2.B * w2.Cout < 1024 or (args.no_others and name != args.workload):
                 continue
             log(f"nhwc {name}")
             g2 = gpu_inputs(torch, w2, dev, seed=0)
