@@ -586,7 +586,9 @@ __global__ void __launch_bounds__(G::NTHR)
     float bv = pad, pv = 0.0f;
     if (real) {
       bv = a.b[co];
-      if constexpr (EPI == EPI_MUL_LRELU_GELU || EPI == EPI_MUL_LRELU_GELU_TANH)
+      if constexpr (EPI == EPI_MUL_LRELU_GELU)
+        pv = a.v0[co] * kGeluIn;  // (the folded form of mul_lrelu_gelu_erf)
+      if constexpr (EPI == EPI_MUL_LRELU_GELU_TANH)
         pv = a.v0[co];
       if constexpr (EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH)
         pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : -1.0f;
@@ -743,11 +745,12 @@ __global__ void __launch_bounds__(G::NTHR)
         pix_off[j] = (uint32_t)(r * a.Wo + c) * (G::NHWC ? (uint32_t)a.Cout : 1u);
         drop[j] = (uint32_t)!(col_ok && r < a.Ho) << 31;
       }
+      const bool neg_slope = slope < 0.0f;
       auto op = [&](float y, float mv) X3_INLINE {
-        if constexpr (EPI != EPI_STORE) {
-          const float v = lrelu(y * mv, slope);
-          y = (EPI == EPI_MUL_LRELU_GELU) ? gelu_erf(v) : gelu_tanh(v);
-        }
+        if constexpr (EPI == EPI_MUL_LRELU_GELU)
+          y = mul_lrelu_gelu_erf(y, mv, slope, neg_slope);
+        else if constexpr (EPI == EPI_MUL_LRELU_GELU_TANH)
+          y = gelu_tanh(lrelu(y * mv, slope));
         return y;
       };
       if (G::NHWC && (a.flags & kOutVec4)) {

@@ -131,17 +131,18 @@ struct EwArgs {
 
 constexpr int kEwPerThread = 4;  // float4 (or floats) per thread
 
+// m: the multiplier, times kGeluIn for the erf form (see mul_lrelu_gelu_erf)
 template <bool TANH>
 __device__ __forceinline__ float ew_op(float y, float m, float slope) {
-  const float v = lrelu(y * m, slope);
-  return TANH ? gelu_tanh(v) : gelu_erf(v);
+  if constexpr (TANH) return gelu_tanh(lrelu(y * m, slope));
+  else return mul_lrelu_gelu_erf(y, m, slope, slope < 0.0f);
 }
 
 template <bool TANH, bool VEC>
 __global__ void __launch_bounds__(kEpiThreads) mul_lrelu_gelu_kernel(const EwArgs a) {
   const int64_t plane = blockIdx.x / a.nchunk;  // n * C + c
   const int64_t chunk = blockIdx.x - plane * a.nchunk;
-  const float m = a.mult[plane % a.C];
+  const float m = a.mult[plane % a.C] * (TANH ? 1.0f : kGeluIn);
   const float* src = a.y + plane * a.P;
   float* dst = a.out + plane * a.P;
   const int64_t first = chunk * (kEpiThreads * kEwPerThread) + threadIdx.x;
