@@ -581,6 +581,7 @@ __global__ void __launch_bounds__(G::NTHR)
   if constexpr (EPI == EPI_MIN_TANH2) pad = __builtin_inff();
   if constexpr (EPI == EPI_SCALE_MIN)
     pad = (a.s0 >= 0.0f) ? __builtin_inff() : -__builtin_inff();
+  int dir_neg = 0;  // a channel of this thread keeps its window minimum
   for (int co = tid; co < a.ncb * G::COUT; co += G::NTHR) {
     const bool real = co < a.Cout;
     float bv = pad, pv = 0.0f;
@@ -595,8 +596,15 @@ __global__ void __launch_bounds__(G::NTHR)
     }
     s_bias[co] = bv;
     s_par[co] = pv;
+    dir_neg |= pv < 0.0f;
   }
   // (made visible by the barrier at the top of the first item)
+  // Pooling epilogues: whether every channel keeps its window maximum
+  // (gamma*scale >= 0 throughout, the usual case); then the extrema need
+  // no direction factor.
+  bool all_max = false;
+  if constexpr (EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH)
+    all_max = __builtin_amdgcn_readfirstlane(!__syncthreads_or(dir_neg)) != 0;
 
   f32x16 acc[G::MT][G::NW];
   // running channel extremum of the min epilogues, per N-tile, carried from
@@ -995,39 +1003,54 @@ __global__ void __launch_bounds__(G::NTHR)
       const uint32_t win_bad = (uint32_t)!(py < a.Ph && px < a.Pw) << 31;
       const bool q0 = lane & 1, q1 = (lane >> 1) & 1;
       const int e = 2 * q0 + q1;
+      // SG: per-channel direction factors; without (all_max) the chains
+      // take the raw values.  (one uniform branch around two compile-time
+      // forms)
+      auto extrema = [&](auto sgc) X3_INLINE {
+        constexpr bool SG = decltype(sgc)::value;
 #pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt)
+        for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int cq = co0 + mt * 32 + 8 * q + 4 * h;  // first channel
-          const f32x4 sg = *reinterpret_cast<const f32x4*>(&s_par[cq]);
-          f32x4 t;
+          for (int q = 0; q < 4; ++q) {
+            const int cq = co0 + mt * 32 + 8 * q + 4 * h;  // first channel
+            f32x4 sg = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (SG) sg = *reinterpret_cast<const f32x4*>(&s_par[cq]);
+            f32x4 t;
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            float m = sg[e2] * acc[mt][0][4 * q + e2];
+            for (int e2 = 0; e2 < 4; ++e2) {
+              float m = SG ? sg[e2] * acc[mt][0][4 * q + e2] : acc[mt][0][4 * q + e2];
 #pragma unroll
-            for (int j = 1; j < G::NW; ++j) m = vmax(m, sg[e2] * acc[mt][j][4 * q + e2]);
-            t[e2] = m;
+              for (int j = 1; j < G::NW; ++j)
+                m = vmax(m, SG ? sg[e2] * acc[mt][j][4 * q + e2] : acc[mt][j][4 * q + e2]);
+              t[e2] = m;
+            }
+            f32x2 u = q0 ? t.hi : t.lo;
+            {
+              const f32x2 give = q0 ? t.lo : t.hi;
+#pragma unroll
+              for (int k = 0; k < 2; ++k) u[k] = vmax(u[k], dpp<DPP_QUAD_XOR1>(give[k]));
+            }
+            const float r = vmax(q1 ? u.y : u.x, dpp<DPP_QUAD_XOR2>(q1 ? u.x : u.y));
+            float v = r;
+            if constexpr (SG) {
+              const f32x2 s2 = q0 ? sg.hi : sg.lo;
+              v = (q1 ? s2.y : s2.x) * r;
+            }
+            const int co = cq + e;
+            // NCHW: channel planes (padded channels fall past the end);
+            // NHWC: channels innermost (padded channels get the drop bit)
+            const uint32_t off =
+                G::NHWC ? ((win_off * (uint32_t)a.Cout + (uint32_t)co) << 2) |
+                              win_bad | ((uint32_t)(co >= a.Cout) << 31)
+                        : (((uint32_t)co * PP + win_off) << 2) | win_bad;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v),
+                                                  o_rsrc, off, 0, 0);
           }
-          f32x2 u = q0 ? t.hi : t.lo;
-          {
-            const f32x2 give = q0 ? t.lo : t.hi;
-#pragma unroll
-            for (int k = 0; k < 2; ++k) u[k] = vmax(u[k], dpp<DPP_QUAD_XOR1>(give[k]));
-          }
-          const float r = vmax(q1 ? u.y : u.x, dpp<DPP_QUAD_XOR2>(q1 ? u.x : u.y));
-          const f32x2 s2 = q0 ? sg.hi : sg.lo;
-          const float v = (q1 ? s2.y : s2.x) * r;
-          const int co = cq + e;
-          // NCHW: channel planes (padded channels fall past the end);
-          // NHWC: channels innermost (padded channels get the drop bit)
-          const uint32_t off =
-              G::NHWC ? ((win_off * (uint32_t)a.Cout + (uint32_t)co) << 2) |
-                            win_bad | ((uint32_t)(co >= a.Cout) << 31)
-                      : (((uint32_t)co * PP + win_off) << 2) | win_bad;
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v),
-                                                o_rsrc, off, 0, 0);
-        }
+      };
+      if (all_max)
+        extrema(std::false_type{});
+      else
+        extrema(std::true_type{});
     }
   };
 
@@ -1304,15 +1327,22 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
   const float4* p = a.part + (size_t)ng * a.pps;
 
   const float4 p0 = tid < a.pps ? p[tid] : make_float4(0.f, 0.f, 0.f, 0.f);
-  // this thread's first block element, requested now so that its latency
-  // hides behind the statistics merge below
-  float4 first = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (tid < nvec) {
-    if constexpr (VEC)
-      first = reinterpret_cast<const float4*>(o)[tid];
-    else
-      first.x = o[tid];
-  }
+  // This thread's first 4 block elements (float4 or float), requested now
+  // so that their latency hides behind the statistics merge below and the
+  // normalize loop waits on no load (the pooled block of a group of 4
+  // channels of 31x31 is 961 float4: at most 4 per thread).
+  auto load = [&](int k) X3_INLINE {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < nvec) {
+      if constexpr (VEC)
+        v = reinterpret_cast<const float4*>(o)[k];
+      else
+        v.x = o[k];
+    }
+    return v;
+  };
+  const float4 pre0 = load(tid), pre1 = load(tid + NT), pre2 = load(tid + 2 * NT),
+               pre3 = load(tid + 3 * NT);
   float mu, rstd;
   gn_group_stats<NT>(a, p, p0, red0, red1, mu, rstd);
 
@@ -1352,20 +1382,20 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
                    (e) < p1 ? B0 : ((e) < p2 ? B1 : ((e) < p3 ? B2 : B3))), \
               lo),                                                          \
         hi)
-  for (int k = tid; k < nvec; k += NT) {
+  // (one loop: the first 4 trips take the prefetched values)
+#pragma unroll 4
+  for (int r = 0, k = tid; k < nvec; ++r, k += NT) {
+    const float4 v = r == 0 ? pre0 : (r == 1 ? pre1 : (r == 2 ? pre2 : (r == 3 ? pre3 : load(k))));
     if constexpr (VEC) {
-      const float4 v =
-          k == tid ? first : reinterpret_cast<const float4*>(o)[k];
       const int e = 4 * k;
-      float4 r;
-      r.x = X3_GN_OUT(v.x, e);
-      r.y = X3_GN_OUT(v.y, e + 1);
-      r.z = X3_GN_OUT(v.z, e + 2);
-      r.w = X3_GN_OUT(v.w, e + 3);
-      reinterpret_cast<float4*>(o)[k] = r;
+      float4 q;
+      q.x = X3_GN_OUT(v.x, e);
+      q.y = X3_GN_OUT(v.y, e + 1);
+      q.z = X3_GN_OUT(v.z, e + 2);
+      q.w = X3_GN_OUT(v.w, e + 3);
+      reinterpret_cast<float4*>(o)[k] = q;
     } else {
-      const float v = k == tid ? first.x : o[k];
-      o[k] = X3_GN_OUT(v, k);
+      o[k] = X3_GN_OUT(v.x, k);
     }
   }
 #undef X3_GN_OUT
@@ -1374,10 +1404,16 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
 // The finalize for pooled extrema stored NHWC, out [B][Ph][Pw][C]: the
 // channels of one pooled position are contiguous, so a workgroup takes a
 // contiguous chunk of one sample's [plane][C] block (all groups) and moves
-// it with 16-byte accesses (VEC: C % 4 == 0, out 16-byte aligned).  It
-// first merges the statistics of every group of the sample (one wavefront
-// per group at a time; the partials are few and L2-resident) into
-// per-channel constants in LDS.
+// it with 16-byte accesses (VEC: C % 4 == 0, out 16-byte aligned).  Its
+// chunk is requested first; meanwhile the workgroup merges the statistics
+// of every group of the sample (one wavefront per group at a time; the
+// partials are few and L2-resident) into per-channel constants in LDS.
+// The merge is one pass over the partials in double: with s_k = sum_k,
+// N = sum n_k, mean = sum s_k / N and
+//   M2 = sum_k M2_k + sum_k n_k (s_k/n_k - mean)^2
+//      = sum_k (M2_k + s_k^2 / n_k) - (sum s_k)^2 / N,
+// the same sum as the pairwise (Chan) combination, reordered so that each
+// partial is read once.
 template <int NT>
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
@@ -1385,27 +1421,46 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-constexpr int kFinNhwcPerThread = 8;  // float4 (or floats) per thread
+constexpr int kFinNhwcThreads = 512;
+constexpr int kFinNhwcPerThread = 4;  // float4 (or floats) per thread
 
 template <int NT, bool VEC>
 __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a) {
   __shared__ float s_mu[kMaxCout], s_A[kMaxCout], s_B[kMaxCout];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = blockIdx.x / a.nchunk, chunk = blockIdx.x - n * a.nchunk;
+  float* o = a.out + (size_t)n * a.plane * a.C;
+  const int total = a.plane * a.C;
+  const int span = NT * kFinNhwcPerThread;
+  const int nel = VEC ? total / 4 : total;
+  const int beg = chunk * span;
+  const int end = min(beg + span, nel);
+  float4 pre[kFinNhwcPerThread];
+#pragma unroll
+  for (int r = 0; r < kFinNhwcPerThread; ++r) {
+    const int k = beg + tid + r * NT;
+    pre[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < end) {
+      if constexpr (VEC)
+        pre[r] = reinterpret_cast<const float4*>(o)[k];
+      else
+        pre[r].x = o[k];
+    }
+  }
   for (int g = wave; g < a.groups; g += NT / 64) {
     const float4* p = a.part + ((size_t)n * a.groups + g) * a.pps;
-    double sum = 0.0;
-    for (int k = lane; k < a.pps; k += 64) sum += (double)p[k].x;
-    const double mean = wave_sum_d<NT>(sum) / a.count;
-    double m2 = 0.0;
+    double sum = 0.0, sq = 0.0;
     for (int k = lane; k < a.pps; k += 64) {
       const float4 v = p[k];
       if (v.z > 0.0f) {
-        const double d = (double)v.x / (double)v.z - mean;
-        m2 += (double)v.y + (double)v.z * d * d;
+        sum += (double)v.x;
+        sq += (double)v.y + (double)v.x * (double)v.x / (double)v.z;
       }
     }
-    m2 = wave_sum_d<NT>(m2);
+    sum = wave_sum_d<NT>(sum);
+    sq = wave_sum_d<NT>(sq);
+    const double mean = sum / a.count;
+    const double m2 = fmax(sq - sum * mean, 0.0);
     const float rstd = (float)(1.0 / sqrt(m2 / a.count + (double)a.eps));
     for (int c = g * a.cpg + lane; c < (g + 1) * a.cpg; c += 64) {
       s_mu[c] = (float)mean;
@@ -1414,26 +1469,21 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
     }
   }
   __syncthreads();
-  float* o = a.out + (size_t)n * a.plane * a.C;
-  const int total = a.plane * a.C;
-  const int span = NT * kFinNhwcPerThread;
-  if constexpr (VEC) {
-    float4* o4 = reinterpret_cast<float4*>(o);
-    const int end = min((chunk + 1) * span, total / 4);
-    for (int k = chunk * span + tid; k < end; k += NT) {
+#pragma unroll
+  for (int r = 0; r < kFinNhwcPerThread; ++r) {
+    const int k = beg + tid + r * NT;
+    if (k >= end) continue;
+    if constexpr (VEC) {
       const int c = (4 * k) % a.C;  // 4 consecutive channels (C % 4 == 0)
-      float4 v = o4[k];
+      float4 v = pre[r];
       v.x = fminf(fmaxf(fmaf(v.x - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
       v.y = fminf(fmaxf(fmaf(v.y - s_mu[c + 1], s_A[c + 1], s_B[c + 1]), a.lo), a.hi);
       v.z = fminf(fmaxf(fmaf(v.z - s_mu[c + 2], s_A[c + 2], s_B[c + 2]), a.lo), a.hi);
       v.w = fminf(fmaxf(fmaf(v.w - s_mu[c + 3], s_A[c + 3], s_B[c + 3]), a.lo), a.hi);
-      o4[k] = v;
-    }
-  } else {
-    const int end = min((chunk + 1) * span, total);
-    for (int k = chunk * span + tid; k < end; k += NT) {
+      reinterpret_cast<float4*>(o)[k] = v;
+    } else {
       const int c = k % a.C;
-      o[k] = fminf(fmaxf(fmaf(o[k] - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
+      o[k] = fminf(fmaxf(fmaf(pre[r].x - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
     }
   }
 }

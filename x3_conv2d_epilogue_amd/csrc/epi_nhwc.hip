@@ -85,17 +85,17 @@ x3_status launch_nhwc(const x3::ConvArgs& a, int epi, hipStream_t st) {
 x3_status launch_gn_finalize_nhwc(x3::GnFinArgs f, int B, hipStream_t st) {
   const bool vec = f.C % 4 == 0 && ((uintptr_t)f.out & 15u) == 0;
   const int64_t per = (int64_t)f.plane * f.C / (vec ? 4 : 1);
-  const int64_t span = 256 * x3::kFinNhwcPerThread;
+  const int64_t span = (int64_t)x3::kFinNhwcThreads * x3::kFinNhwcPerThread;
   f.nchunk = (int)((per + span - 1) / span);
   const int64_t blocks = (int64_t)B * f.nchunk;
   if (blocks >= (1ll << 31) || (int64_t)f.plane * f.C >= (1ll << 31))
     return fail(X3_EUNSUPPORTED, "pooled output too large for one launch");
   if (vec)
-    hipLaunchKernelGGL((x3::gn_finalize_nhwc_kernel<256, true>), dim3((unsigned)blocks),
-                       dim3(256), 0, st, f);
+    hipLaunchKernelGGL((x3::gn_finalize_nhwc_kernel<x3::kFinNhwcThreads, true>),
+                       dim3((unsigned)blocks), dim3(x3::kFinNhwcThreads), 0, st, f);
   else
-    hipLaunchKernelGGL((x3::gn_finalize_nhwc_kernel<256, false>), dim3((unsigned)blocks),
-                       dim3(256), 0, st, f);
+    hipLaunchKernelGGL((x3::gn_finalize_nhwc_kernel<x3::kFinNhwcThreads, false>),
+                       dim3((unsigned)blocks), dim3(x3::kFinNhwcThreads), 0, st, f);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(X3_EHIP, "finalize kernel launch failed: %s",
