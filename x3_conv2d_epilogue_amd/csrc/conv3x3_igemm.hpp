@@ -1327,22 +1327,15 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
   const float4* p = a.part + (size_t)ng * a.pps;
 
   const float4 p0 = tid < a.pps ? p[tid] : make_float4(0.f, 0.f, 0.f, 0.f);
-  // This thread's first 4 block elements (float4 or float), requested now
-  // so that their latency hides behind the statistics merge below and the
-  // normalize loop waits on no load (the pooled block of a group of 4
-  // channels of 31x31 is 961 float4: at most 4 per thread).
-  auto load = [&](int k) X3_INLINE {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < nvec) {
-      if constexpr (VEC)
-        v = reinterpret_cast<const float4*>(o)[k];
-      else
-        v.x = o[k];
-    }
-    return v;
-  };
-  const float4 pre0 = load(tid), pre1 = load(tid + NT), pre2 = load(tid + 2 * NT),
-               pre3 = load(tid + 3 * NT);
+  // this thread's first block element, requested now so that its latency
+  // hides behind the statistics merge below
+  float4 first = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (tid < nvec) {
+    if constexpr (VEC)
+      first = reinterpret_cast<const float4*>(o)[tid];
+    else
+      first.x = o[tid];
+  }
   float mu, rstd;
   gn_group_stats<NT>(a, p, p0, red0, red1, mu, rstd);
 
@@ -1382,20 +1375,20 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
                    (e) < p1 ? B0 : ((e) < p2 ? B1 : ((e) < p3 ? B2 : B3))), \
               lo),                                                          \
         hi)
-  // (one loop: the first 4 trips take the prefetched values)
-#pragma unroll 4
-  for (int r = 0, k = tid; k < nvec; ++r, k += NT) {
-    const float4 v = r == 0 ? pre0 : (r == 1 ? pre1 : (r == 2 ? pre2 : (r == 3 ? pre3 : load(k))));
+  for (int k = tid; k < nvec; k += NT) {
     if constexpr (VEC) {
+      const float4 v =
+          k == tid ? first : reinterpret_cast<const float4*>(o)[k];
       const int e = 4 * k;
-      float4 q;
-      q.x = X3_GN_OUT(v.x, e);
-      q.y = X3_GN_OUT(v.y, e + 1);
-      q.z = X3_GN_OUT(v.z, e + 2);
-      q.w = X3_GN_OUT(v.w, e + 3);
-      reinterpret_cast<float4*>(o)[k] = q;
+      float4 r;
+      r.x = X3_GN_OUT(v.x, e);
+      r.y = X3_GN_OUT(v.y, e + 1);
+      r.z = X3_GN_OUT(v.z, e + 2);
+      r.w = X3_GN_OUT(v.w, e + 3);
+      reinterpret_cast<float4*>(o)[k] = r;
     } else {
-      o[k] = X3_GN_OUT(v.x, k);
+      const float v = k == tid ? first.x : o[k];
+      o[k] = X3_GN_OUT(v, k);
     }
   }
 #undef X3_GN_OUT
@@ -1404,10 +1397,12 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
 // The finalize for pooled extrema stored NHWC, out [B][Ph][Pw][C]: the
 // channels of one pooled position are contiguous, so a workgroup takes a
 // contiguous chunk of one sample's [plane][C] block (all groups) and moves
-// it with 16-byte accesses (VEC: C % 4 == 0, out 16-byte aligned).  Its
-// chunk is requested first; meanwhile the workgroup merges the statistics
-// of every group of the sample (one wavefront per group at a time; the
-// partials are few and L2-resident) into per-channel constants in LDS.
+// it with 16-byte accesses (VEC: C % 4 == 0, out 16-byte aligned), after
+// merging the statistics of every group of the sample (one wavefront per
+// group at a time; the partials are few and L2-resident) into per-channel
+// constants in LDS.  (Requesting the chunk before the merge was measured
+// slower: those loads then queue ahead of the partials the merge waits
+// for.)
 // The merge is one pass over the partials in double: with s_k = sum_k,
 // N = sum n_k, mean = sum s_k / N and
 //   M2 = sum_k M2_k + sum_k n_k (s_k/n_k - mean)^2
@@ -1435,18 +1430,6 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
   const int nel = VEC ? total / 4 : total;
   const int beg = chunk * span;
   const int end = min(beg + span, nel);
-  float4 pre[kFinNhwcPerThread];
-#pragma unroll
-  for (int r = 0; r < kFinNhwcPerThread; ++r) {
-    const int k = beg + tid + r * NT;
-    pre[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < end) {
-      if constexpr (VEC)
-        pre[r] = reinterpret_cast<const float4*>(o)[k];
-      else
-        pre[r].x = o[k];
-    }
-  }
   for (int g = wave; g < a.groups; g += NT / 64) {
     const float4* p = a.part + ((size_t)n * a.groups + g) * a.pps;
     double sum = 0.0, sq = 0.0;
@@ -1475,7 +1458,7 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
     if (k >= end) continue;
     if constexpr (VEC) {
       const int c = (4 * k) % a.C;  // 4 consecutive channels (C % 4 == 0)
-      float4 v = pre[r];
+      float4 v = reinterpret_cast<const float4*>(o)[k];
       v.x = fminf(fmaxf(fmaf(v.x - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
       v.y = fminf(fmaxf(fmaf(v.y - s_mu[c + 1], s_A[c + 1], s_B[c + 1]), a.lo), a.hi);
       v.z = fminf(fmaxf(fmaf(v.z - s_mu[c + 2], s_A[c + 2], s_B[c + 2]), a.lo), a.hi);
@@ -1483,7 +1466,7 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
       reinterpret_cast<float4*>(o)[k] = v;
     } else {
       const int c = k % a.C;
-      o[k] = fminf(fmaxf(fmaf(pre[r].x - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
+      o[k] = fminf(fmaxf(fmaf(o[k] - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
     }
   }
 }
