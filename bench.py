@@ -250,6 +250,9 @@ def main():
                     help="skip the unfused (conv + standalone epilogue) comparison")
     ap.add_argument("--no-nhwc", action="store_true",
                     help="skip timing the NHWC (channels_last) forms of the workloads")
+    ap.add_argument("--copy-ref-mib", type=int, default=1024,
+                    help="time a plain device-to-device copy of this size as the practical "
+                         "HBM reference for the standalone epilogues (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -385,6 +388,21 @@ def main():
             del g2, o2, ws2, op2
             torch.cuda.empty_cache()
 
+    # The practical HBM ceiling of a read+write stream on this machine: a plain
+    # device-to-device copy (the runtime's copy kernel), large enough to
+    # miss the 256 MB last-level cache.
+    copy_ref = None
+    if args.copy_ref_mib > 0:
+        n = args.copy_ref_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        _, cms = time_op(torch, lambda: dst.copy_(src), 20, 3)
+        gbps = 2 * 4 * n / (cms * 1e-3) / 1e9
+        copy_ref = {"mib": args.copy_ref_mib, "ms": round(cms, 4), "GBps": round(gbps, 1),
+                    "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        del src, dst
+        torch.cuda.empty_cache()
+
     cpu = None
     parity = None
     if args.cpu_budget > 0:
@@ -415,6 +433,7 @@ def main():
         "other_workloads": others,
         "unfused_ablation": abl,
         "nhwc_workloads": nhwc,
+        "copy_reference": copy_ref,
         "host": {"cpu": platform.processor() or platform.machine(), "cpu_count": os.cpu_count(),
                  "device": torch.cuda.get_device_name(0)},
     }

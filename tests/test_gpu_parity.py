@@ -190,6 +190,19 @@ def test_gn_pool_all_ones_closed_form():
                  what="all ones")
 
 
+def test_gn_pool_samples_of_different_scales():
+    """Samples whose conv outputs differ in scale by 10^4 and in offset:
+    every sample's statistics must follow from its own values.  With 48
+    samples of 8 row tiles each there are more tiles than workgroups, so a
+    workgroup handles tiles of samples of very different scales in turn."""
+    d = random_case("gn_scale_pool_clamp", 48, 8, 34, 34, 64, seed=603)
+    d["x"][0::2] *= 1e-3
+    d["x"][1::2] = d["x"][1::2] * 10.0 + 5.0
+    kw = dict(lo=-100.0, hi=100.0)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw), run_oracle("gn_scale_pool_clamp", d, **kw),
+                 what="per-sample scales")
+
+
 def test_edge_minimal_spatial():
     """H = W = 3: a single output pixel per sample."""
     d = random_case("min_tanh2", 3, 7, 3, 3, 64, seed=700)
