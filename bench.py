@@ -258,7 +258,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
+        print(f"bench.py: this benchmark runs on exactly one GPU (asked for {args.gpus}); "
               "the multi-GPU path is design-only (batch sharding, no collectives).",
               file=sys.stderr)
         sys.exit(2)
