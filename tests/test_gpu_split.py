@@ -107,6 +107,27 @@ def test_epi_gn_any_pool(k, cg, hw):
     assert_close(got, ref, what=f"k={k}")
 
 
+@pytest.mark.parametrize("groups", [1, 4])
+def test_epi_gn_pooled_block_beyond_lds(groups):
+    """4x4 windows on even rows: a group whose pooled block fits the LDS
+    budget (groups=4: one 64x64 pooled plane) runs in the one-kernel group
+    form; a group of 4 such planes (groups=1) does not, and takes the plane
+    kernel plus the finalize."""
+    shape = (1, 4, 258, 256)
+    say(f"epi gn {shape} groups={groups} k=4")
+    y, x, w, b = identity_case(*shape, seed=300 + groups)
+    g = torch.Generator().manual_seed(30 + groups)
+    gamma = (1.0 + 0.2 * torch.randn(4, generator=g)).float()
+    gamma[1] *= -1.0
+    beta = (0.1 * torch.randn(4, generator=g)).float()
+    scale = (1.0 + 0.2 * torch.randn(4, generator=g)).float()
+    got = x3.epi_gn_scale_pool_clamp(y.to(DEV), gamma.to(DEV), beta.to(DEV), scale.to(DEV),
+                                     groups, 1e-5, 4, -2.0, 2.0)
+    ref = oracle.gn_scale_pool_clamp(x, w, b, gamma.numpy(), beta.numpy(), scale.numpy(),
+                                     groups, 1e-5, 4, -2.0, 2.0)
+    assert_close(got, ref, what=f"groups={groups}")
+
+
 SHAPES = [(2, 16, 32, 32), (1, 12, 20, 67), (1, 16, 11, 131), (1, 20, 7, 300)]
 
 

@@ -74,6 +74,30 @@ x3_status launch_epi_gn(const x3::GnPlaneArgs& g, int64_t B, int groups,
   if (planes >= (1ll << 31) || B * groups >= (1ll << 31))
     return fail(X3_EUNSUPPORTED, "too many planes for one launch");
   const dim3 grid((unsigned)planes), block(x3::kEpiThreads);
+  const int cpg = g.C / groups;
+  const int64_t ext_bytes = (int64_t)cpg * g.Ph * g.Pw * 4;
+  if (g.k == 4 && g.W % 2 == 0 && ((uintptr_t)g.y & 7u) == 0 &&
+      cpg <= x3::kGnGroupMaxCpg && ext_bytes <= x3::kGnGroupMaxLdsBytes) {
+    // one kernel: statistics, extrema and normalization per (sample, group)
+    x3::GnGroupArgs q{};
+    q.y = g.y;
+    q.gamma = g.gamma;
+    q.beta = beta;
+    q.scale = g.scale;
+    q.out = g.out;
+    q.C = g.C;
+    q.H = g.H;
+    q.W = g.W;
+    q.Ph = g.Ph;
+    q.Pw = g.Pw;
+    q.cpg = cpg;
+    q.eps = eps;
+    q.lo = lo;
+    q.hi = hi;
+    hipLaunchKernelGGL((x3::gn_group_k4w2_kernel<4>), dim3((unsigned)(B * groups)), block,
+                       (unsigned)ext_bytes, st, q);
+    return launched("GroupNorm group kernel");
+  }
   if (g.k == 4 && g.W % 2 == 0 && ((uintptr_t)g.y & 7u) == 0)
     hipLaunchKernelGGL((x3::gn_plane_k4w2_kernel<4>), grid, block, 0, st, g);
   else if (g.k == 4)

@@ -455,4 +455,157 @@ __global__ void __launch_bounds__(kEpiThreads) gn_plane_k4w2_kernel(const GnPlan
   }
 }
 
+// The whole GroupNorm epilogue in one kernel, one workgroup per (sample,
+// group), for 4x4 windows, an even row length and a group whose pooled
+// block (cpg * Ph * Pw floats) fits the dynamic LDS: wavefront w walks the
+// group's planes w, w + NWV, ... as gn_plane_k4w2_kernel does (8-byte
+// loads, 3 units in flight, within 64 registers for 8 wavefronts per SIMD)
+// and parks each window's extremum in LDS instead
+// of in out.  Each plane's (sum, M2) about its own first element is
+// reduced over the wavefront in double; the group's mean and variance
+// follow from the pairwise (Chan) combination of its planes; the parked
+// extrema are then normalized, scaled and clamped on their way to out.  y
+// is read once and out written once, with no workspace and no second
+// kernel.
+#define X3_EPI_INLINE __attribute__((always_inline))
+constexpr int kGnGroupMaxCpg = 64;
+constexpr int kGnGroupMaxLdsBytes = 48 * 1024;
+
+struct GnGroupArgs {
+  const float* y;
+  const float* gamma;
+  const float* beta;
+  const float* scale;
+  float* out;  // [B][C][Ph][Pw]
+  int C, H, W, Ph, Pw, cpg;
+  float eps, lo, hi;
+};
+
+__device__ __forceinline__ double wave_sum64_d(double v) {
+#pragma unroll
+  for (int mask = 1; mask < 64; mask <<= 1) v += __shfl_xor(v, mask, 64);
+  return v;
+}
+
+// (a template only so that every translation unit may include it)
+template <int K4 = 4>
+__global__ void __launch_bounds__(kEpiThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+gn_group_k4w2_kernel(const GnGroupArgs a) {
+  constexpr int NT = kEpiThreads, NWV = NT / 64;
+  extern __shared__ float s_ext[];  // [cpg][Ph*Pw] parked extrema
+  __shared__ double s_ps[kGnGroupMaxCpg], s_pm[kGnGroupMaxCpg];
+  __shared__ float s_A[kGnGroupMaxCpg], s_B[kGnGroupMaxCpg];
+  __shared__ float s_mu;
+  const int groups = a.C / a.cpg;
+  const int n = blockIdx.x / groups, g = blockIdx.x - n * groups;
+  const int c0 = g * a.cpg;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.H * a.W, PP = a.Ph * a.Pw;
+  const int cw = a.Pw * 4, rh = a.Ph * 4;
+  const int nsx = (a.W + 127) / 128;  // 128-column steps per row band
+  const int nunits = a.Ph * nsx;
+  for (int pl = wave; pl < a.cpg; pl += NWV) {
+    const int c = c0 + pl;
+    const float* yb = a.y + ((int64_t)n * a.C + c) * P;
+    float* eb = s_ext + pl * PP;
+    const bool keep_max = (a.gamma[c] >= 0.0f) == (a.scale[c] >= 0.0f);
+    const float Kf = yb[0];
+    float s1 = 0.0f, s2 = 0.0f;
+    constexpr int UNR = 3;  // units in flight (4 would exceed 64 registers)
+    for (int u0 = 0; u0 < nunits; u0 += UNR) {
+      float2 v[UNR][4];
+      // unit u: row band py, this lane's first column x (recomputed after
+      // the loads rather than kept: registers bound the occupancy here)
+      auto unit = [&](int u, int& py, int& x) X3_EPI_INLINE {
+        py = u / nsx;
+        x = (u - py * nsx) * 128 + 2 * lane;
+        return u < nunits && x < a.W;  // (W even: x + 1 < W too)
+      };
+#pragma unroll
+      for (int q = 0; q < UNR; ++q) {
+        int py, x;
+        const bool ok = unit(u0 + q, py, x);
+        // (a unit past the end, or a lane past the row, reads the plane's
+        // first two columns instead: no load leaves the plane)
+        const float* src = yb + (ok ? py * 4 * a.W + x : 0);
+#pragma unroll
+        for (int dy = 0; dy < 4; ++dy)
+          v[q][dy] = *reinterpret_cast<const float2*>(src + dy * a.W);
+      }
+#pragma unroll
+      for (int q = 0; q < UNR; ++q) {
+        int py, x;
+        const bool ok = unit(u0 + q, py, x);
+        float mx = -__builtin_inff(), mn = __builtin_inff();
+#pragma unroll
+        for (int dy = 0; dy < 4; ++dy) {
+          const float d0 = ok ? v[q][dy].x - Kf : 0.0f;
+          const float d1 = ok ? v[q][dy].y - Kf : 0.0f;
+          s1 += d0 + d1;
+          s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
+          mx = fmaxf(mx, fmaxf(v[q][dy].x, v[q][dy].y));
+          mn = fminf(mn, fminf(v[q][dy].x, v[q][dy].y));
+        }
+        // the 2 lanes of a window are an even/odd pair
+        mx = fmaxf(mx, quad_swap<0xB1>(mx));
+        mn = fminf(mn, quad_swap<0xB1>(mn));
+        if (ok && (lane & 1) == 0 && x + 3 < cw) eb[py * a.Pw + x / 4] = keep_max ? mx : mn;
+      }
+    }
+    // the rows below the last window, for the statistics (8-byte pairs)
+    const int half = a.W / 2;
+    const int rem = (a.H - rh) * half;
+    for (int e0 = lane; e0 < rem; e0 += 4 * 64) {
+      float2 w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + q * 64 < rem ? e0 + q * 64 : 0;
+        w[q] = *reinterpret_cast<const float2*>(yb + rh * a.W + 2 * e);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = e0 + q * 64 < rem;
+        const float d0 = ok ? w[q].x - Kf : 0.0f, d1 = ok ? w[q].y - Kf : 0.0f;
+        s1 += d0 + d1;
+        s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
+      }
+    }
+    const double S1 = wave_sum64_d((double)s1);
+    const double S2 = wave_sum64_d((double)s2);
+    if (lane == 0) {
+      const double np = (double)P;
+      s_ps[pl] = np * (double)Kf + S1;        // the plane's sum
+      s_pm[pl] = fmax(S2 - S1 * S1 / np, 0.0);  // its M2 about its mean
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // Chan: M2 = sum_p [M2_p + P (mean_p - mean)^2], all planes of P elements
+    const double np = (double)P, total = np * a.cpg;
+    const bool has = lane < a.cpg;
+    const double mean = wave_sum64_d(has ? s_ps[lane] : 0.0) / total;
+    double t = 0.0;
+    if (has) {
+      const double dm = s_ps[lane] / np - mean;
+      t = s_pm[lane] + np * dm * dm;
+    }
+    const double m2 = wave_sum64_d(t);
+    const float rstd = (float)(1.0 / sqrt(m2 / total + (double)a.eps));
+    if (has) {
+      const int c = c0 + lane;
+      s_A[lane] = rstd * a.gamma[c] * a.scale[c];
+      s_B[lane] = a.beta[c] * a.scale[c];
+    }
+    if (lane == 0) s_mu = (float)mean;
+  }
+  __syncthreads();
+  const float mu = s_mu;
+  float* ob = a.out + ((int64_t)n * a.C + c0) * PP;
+  for (int pl = 0; pl < a.cpg; ++pl) {
+    const float A = s_A[pl], Bc = s_B[pl];
+    for (int k = tid; k < PP; k += NT)
+      ob[pl * PP + k] = fminf(fmaxf(fmaf(s_ext[pl * PP + k] - mu, A, Bc), a.lo), a.hi);
+  }
+}
+
 }  // namespace x3
