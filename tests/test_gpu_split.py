@@ -84,6 +84,26 @@ def test_epi_mul_lrelu_gelu_both_forms(shape):
     assert_close(y2, oracle.mul_lrelu_gelu(x, w, b, mn, 0.01), what="erf in place")
 
 
+@pytest.mark.parametrize("shape", [(2, 6, 64, 66), (1, 3, 128, 128)])
+def test_epi_mul_lrelu_gelu_flat_blocks(shape):
+    """Planes of at least 1024 float4 take the flat form: whole 16 KB blocks
+    over the tensor, a block meeting two planes (P/4 = 1056) or exactly
+    aligned to them (P/4 = 4096)."""
+    say(f"epi gelu flat {shape}")
+    y, x, w, b = identity_case(*shape, seed=400 + sum(shape))
+    g = torch.Generator().manual_seed(8)
+    m = (1.0 + 0.3 * torch.randn(shape[1], generator=g)).float()
+    yd, md = y.to(DEV), m.to(DEV)
+    mn = m.numpy()
+    assert_close(x3.epi_mul_lrelu_gelu(yd, md, 0.01), oracle.mul_lrelu_gelu(x, w, b, mn, 0.01),
+                 what="erf")
+    assert_close(x3.epi_mul_lrelu_gelu_tanh(yd, md, -0.3),
+                 oracle.mul_lrelu_gelu_tanh(x, w, b, mn, -0.3), what="tanh")
+    y2 = yd.clone()
+    x3.epi_mul_lrelu_gelu(y2, md, 0.01, out=y2)
+    assert_close(y2, oracle.mul_lrelu_gelu(x, w, b, mn, 0.01), what="erf in place")
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 7])
 @pytest.mark.parametrize("cg", [(16, 4), (12, 3), (8, 8), (6, 1)])
 @pytest.mark.parametrize("hw", [(23, 29), (22, 30), (13, 260)])

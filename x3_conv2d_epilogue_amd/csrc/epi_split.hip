@@ -48,6 +48,20 @@ x3_status launch_epi_ew(x3::EwArgs e, bool tanh_form, int64_t planes,
   const bool vec = e.P % 4 == 0 && aligned16(e.y) && aligned16(e.out);
   const int64_t per = vec ? e.P / 4 : e.P;
   const int64_t span = (int64_t)x3::kEpiThreads * x3::kEwPerThread;
+  if (vec && per >= span) {
+    // flat form: whole 16 KB blocks over the tensor (see the kernel)
+    e.total4 = per * planes;
+    const int64_t nblk = (e.total4 + span - 1) / span;
+    if (nblk >= (1ll << 31))
+      return fail(X3_EUNSUPPORTED, "too many elements for one launch");
+    if (tanh_form)
+      hipLaunchKernelGGL((x3::mul_lrelu_gelu_flat4_kernel<true>), dim3((unsigned)nblk),
+                         dim3(x3::kEpiThreads), 0, st, e);
+    else
+      hipLaunchKernelGGL((x3::mul_lrelu_gelu_flat4_kernel<false>), dim3((unsigned)nblk),
+                         dim3(x3::kEpiThreads), 0, st, e);
+    return launched("elementwise epilogue kernel");
+  }
   e.nchunk = (per + span - 1) / span;
   const int64_t blocks = planes * e.nchunk;
   if (blocks >= (1ll << 31))

@@ -126,6 +126,7 @@ struct EwArgs {
   int C;
   int64_t P;        // elements per channel plane
   int64_t nchunk;   // blocks per plane
+  int64_t total4;   // flat form: float4 in the whole tensor
   float slope;
 };
 
@@ -179,6 +180,46 @@ __global__ void __launch_bounds__(kEpiThreads) mul_lrelu_gelu_kernel(const EwArg
     for (int k = 0; k < kEwPerThread; ++k) {
       const int64_t e = first + k * kEpiThreads;
       if (e < a.P) dst[e] = ew_op<TANH>(v[k], m, a.slope);
+    }
+  }
+}
+
+// The same operation over the tensor as one flat float4 array (P % 4 == 0,
+// both buffers 16-byte aligned, P / 4 >= the block's span): block b takes
+// the float4 [b*span, (b+1)*span), so every block is full (except the
+// tensor's last) and starts on a 16 KB boundary; a float4 never straddles
+// two planes and a block meets at most two, whose multipliers it reads
+// once.  Measured 10 % faster than the per-plane blocks on [64,64,254,254]
+// (whose last block in each plane is three-quarters full).
+template <bool TANH>
+__global__ void __launch_bounds__(kEpiThreads) mul_lrelu_gelu_flat4_kernel(const EwArgs a) {
+  constexpr int SPAN = kEpiThreads * kEwPerThread;
+  const int64_t per = a.P / 4;
+  const int64_t b0 = (int64_t)blockIdx.x * SPAN;
+  const int64_t plane0 = b0 / per;
+  const int64_t qb = (plane0 + 1) * per;  // first float4 of the next plane
+  const float k = TANH ? 1.0f : kGeluIn;
+  const float m0 = a.mult[plane0 % a.C] * k;
+  const float m1 = a.mult[(plane0 + 1) % a.C] * k;
+  const float4* s4 = reinterpret_cast<const float4*>(a.y);
+  float4* d4 = reinterpret_cast<float4*>(a.out);
+  float4 v[kEwPerThread];
+#pragma unroll
+  for (int r = 0; r < kEwPerThread; ++r) {
+    const int64_t q = b0 + threadIdx.x + r * kEpiThreads;
+    if (q < a.total4) v[r] = ld_stream(s4 + q);
+  }
+#pragma unroll
+  for (int r = 0; r < kEwPerThread; ++r) {
+    const int64_t q = b0 + threadIdx.x + r * kEpiThreads;
+    if (q < a.total4) {
+      const float m = q < qb ? m0 : m1;
+      float4 o;
+      o.x = ew_op<TANH>(v[r].x, m, a.slope);
+      o.y = ew_op<TANH>(v[r].y, m, a.slope);
+      o.z = ew_op<TANH>(v[r].z, m, a.slope);
+      o.w = ew_op<TANH>(v[r].w, m, a.slope);
+      st_stream(o, d4 + q);
     }
   }
 }
