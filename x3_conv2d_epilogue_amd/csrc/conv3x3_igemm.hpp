@@ -66,14 +66,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum Epilogue : int {
   EPI_MIN_TANH2 = 0,       // tanh(tanh(min_co y))
-  EPI_MUL_LRELU_GELU = 1,  // gelu_erf(lrelu(y * mult[co]))
+  EPI_MUL_LRELU_GELU = 1,  // exact GELU(LeakyReLU(y * mult[co]))
   EPI_SCALE_MIN = 2,       // min_co(scale * y)
   EPI_GN_POOL = 3,         // GroupNorm partials per group of 4 channels
                            // + pooling-window extrema
   EPI_GN_POOL_CH = 4,      // GroupNorm partials per channel (any group
                            // size) + pooling-window extrema
   EPI_STORE = 5,           // the conv output itself (split path)
-  EPI_MUL_LRELU_GELU_TANH = 6  // gelu_tanh(lrelu(y * mult[co]))
+  EPI_MUL_LRELU_GELU_TANH = 6  // tanh-form GELU(LeakyReLU(y * mult[co]))
 };
 
 // Kernel arguments (plain values, passed by value).
@@ -1417,7 +1417,7 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 constexpr int kFinNhwcThreads = 512;
-constexpr int kFinNhwcPerThread = 4;  // float4 (or floats) per thread
+constexpr int kFinNhwcPerThread = 8;  // float4 (or floats) per thread
 
 template <int NT, bool VEC>
 __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a) {

@@ -6,53 +6,33 @@
 
 namespace x3 {
 
-// erf for the exact-GELU epilogue, by formula 7.1.26 of Abramowitz and
-// Stegun, Handbook of Mathematical Functions: for x >= 0,
-//   erf(x) ~ 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
-//   t = 1 / (1 + p x),
-// with absolute error at most 1.5e-7; erf is odd.  Costs one reciprocal,
-// one exp2 and six FMAs.
-__device__ __forceinline__ float erf_as(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float q = 1.061405429f;
-  q = fmaf(q, t, -1.453152027f);
-  q = fmaf(q, t, 1.421413741f);
-  q = fmaf(q, t, -0.284496736f);
-  q = fmaf(q, t, 0.254829592f);
-  q *= t;
-  // exp(-x^2) = 2^(-x^2 * log2(e))
-  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-  return copysignf(fmaf(-q, e, 1.0f), x);
-}
-
 // LeakyReLU: v for v >= 0, slope * v otherwise.
 __device__ __forceinline__ float lrelu(float v, float slope) {
   return (v >= 0.0f) ? v : slope * v;
 }
 
-// Exact GELU: v * Phi(v) = 0.5 v (1 + erf(v / sqrt 2)).
-__device__ __forceinline__ float gelu_erf(float v) {
-  return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
-}
-
-// The multiplier -> LeakyReLU -> exact GELU chain with its constant factors
-// folded, for the epilogues that evaluate it on every conv output.  The
-// caller passes mk = m * kGeluIn, kGeluIn = sqrt(log2(e) / 2).  Since
-// LeakyReLU commutes with a positive factor, z = LeakyReLU(y * mk) equals
-// kGeluIn * v with v = LeakyReLU(y * m), and for the erf argument
+// Exact GELU, v * Phi(v) = 0.5 v (1 + erf(v / sqrt 2)), of v =
+// LeakyReLU(y * m), with erf by formula 7.1.26 of Abramowitz and Stegun,
+// Handbook of Mathematical Functions: for x >= 0,
+//   erf(x) ~ 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x),
+// absolute error at most 1.5e-7; erf is odd.  The chain is evaluated with
+// its constant factors folded, for the epilogues that evaluate it on every
+// conv output.  The caller passes mk = m * kGeluIn, kGeluIn =
+// sqrt(log2(e) / 2).  Since LeakyReLU commutes with a positive factor,
+// z = LeakyReLU(y * mk) equals kGeluIn * v, and for the erf argument
 // x = v / sqrt 2:
 //   x^2 log2(e) = z^2, so exp(-x^2) = 2^(-z^2);
 //   t = 1 / (1 + p |x|) = 1 / (1 + p' |z|), p' = p / sqrt(log2 e);
-//   1 + erf(x) = 2 - q e for x >= 0 and q e for x < 0 (formula 7.1.26:
-//   erf |x| = 1 - q e, q = a1 t + ... + a5 t^5, e = exp(-x^2)).
+//   1 + erf(x) = 2 - q e for x >= 0 and q e for x < 0 (erf |x| = 1 - q e,
+//   q = a1 t + ... + a5 t^5, e = exp(-x^2)).
 // GELU(v) = v (1 + erf x) / 2 = z (1 + erf x) / (2 kGeluIn), so with the
 // coefficients scaled by 1 / (2 kGeluIn) (r = q' e):
 //   GELU(v) = z (1 / kGeluIn - r) for x >= 0,  z r for x < 0.
 // x >= 0 exactly when y * mk >= 0 or the slope is negative (neg_slope
 // set): then LeakyReLU maps both signs to z >= 0.  About 15 plain vector
-// operations and 2 transcendentals per element, against 19 and 2 for
-// gelu_erf(lrelu(y * m)).
+// operations and 2 transcendentals (one reciprocal, one exp2) per element,
+// against 19 and 2 for the formula evaluated as written.
 constexpr float kGeluIn = 0.8493218002880191f;  // sqrt(log2(e) / 2)
 
 __device__ __forceinline__ float mul_lrelu_gelu_erf(float y, float mk, float slope,
