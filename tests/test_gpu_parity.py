@@ -136,10 +136,16 @@ def test_scale_min_random_scales(scale):
                  what=f"scale={scale}")
 
 
-def test_mul_lrelu_gelu_other_slope():
+@pytest.mark.parametrize("slope", [0.2, 0.0, -0.5, 1.5])
+def test_mul_lrelu_gelu_other_slope(slope):
+    """Any finite slope: a negative one sends both signs of y*m to a
+    non-negative GELU argument, a slope above 1 keeps negatives negative
+    (the folded exact-GELU form takes the sign of erf's argument from the
+    LeakyReLU compare); the multiplier has both signs."""
     d = random_case("mul_lrelu_gelu", 1, 8, 14, 40, 64, seed=401)
-    assert_close(run_op("mul_lrelu_gelu", d, neg_slope=0.2),
-                 run_oracle("mul_lrelu_gelu", d, neg_slope=0.2), what="slope 0.2")
+    d["multiplier"][::5] *= -1.0
+    assert_close(run_op("mul_lrelu_gelu", d, neg_slope=slope),
+                 run_oracle("mul_lrelu_gelu", d, neg_slope=slope), what=f"slope {slope}")
 
 
 GN_SHAPES = [  # (B, Cin, H, W)

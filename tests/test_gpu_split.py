@@ -99,6 +99,8 @@ def test_epi_mul_lrelu_gelu_flat_blocks(shape):
                  what="erf")
     assert_close(x3.epi_mul_lrelu_gelu_tanh(yd, md, -0.3),
                  oracle.mul_lrelu_gelu_tanh(x, w, b, mn, -0.3), what="tanh")
+    assert_close(x3.epi_mul_lrelu_gelu(yd, md, -0.3), oracle.mul_lrelu_gelu(x, w, b, mn, -0.3),
+                 what="erf, negative slope")
     y2 = yd.clone()
     x3.epi_mul_lrelu_gelu(y2, md, 0.01, out=y2)
     assert_close(y2, oracle.mul_lrelu_gelu(x, w, b, mn, 0.01), what="erf in place")
