@@ -787,6 +787,13 @@ __global__ void __launch_bounds__(G::NTHR)
           }
         return;
       }
+      // NCHW: each store's byte offset is the channel's plane offset plus
+      // the pixel's, one add per store.  A dropped pixel's part is the drop
+      // bit alone, so the add cannot carry out of bit 31 (a channel's
+      // plane offset, padded channels included, is below 2 GiB).
+      uint32_t pixb[G::NW];
+#pragma unroll
+      for (int j = 0; j < G::NW; ++j) pixb[j] = drop[j] ? drop[j] : pix_off[j] << 2;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
@@ -799,9 +806,10 @@ __global__ void __launch_bounds__(G::NTHR)
 #pragma unroll
           for (int j = 0; j < G::NW; ++j) {
             const float y = op(acc[mt][j][i], mv);
-            // (OR, not add: nothing can clear the drop bit)
-            const uint32_t off = ((co_off + pix_off[j]) << 2) | drop[j] |
-                                 (co_off & 0x80000000u);
+            // (NHWC: OR, not add: nothing can clear the drop bits)
+            const uint32_t off =
+                G::NHWC ? ((co_off + pix_off[j]) << 2) | drop[j] | (co_off & 0x80000000u)
+                        : (co_off << 2) + pixb[j];
             __builtin_amdgcn_raw_buffer_store_b32(
                 __builtin_bit_cast(uint32_t, y), o_rsrc, off, 0, 0);
           }
