@@ -153,3 +153,64 @@ def test_nonfinite_input_stays_local(layout):
         err = float(np.abs(got[m] - ref[m]).max())
         say(f"  {layout} {name}: max_abs_err on clean outputs={err:.3e}")
         assert err <= TOL, (name, err)
+
+
+def _pixels(B, Ho, Wo, n, seed):
+    """Edge pixels of the first and last sample plus n random ones."""
+    rng = np.random.default_rng(seed)
+    fixed = [(b, r, c) for b in (0, B - 1) for r in (0, Ho // 2, Ho - 1)
+             for c in (0, 31, 32, 127, 128, Wo - 1) if c < Wo]
+    rand = np.stack([rng.integers(0, B, n), rng.integers(0, Ho, n), rng.integers(0, Wo, n)], 1)
+    return np.concatenate([np.array(fixed), rand]).astype(np.int64)
+
+
+@pytest.mark.parametrize("name", ["min_tanh2", "mul_lrelu_gelu", "scale_min", "gn_pool"])
+def test_nhwc_workloads_full_size(name):
+    """The NHWC form of each benchmark workload at its full size: every
+    output against the NCHW kernel's (whose sampled parity with the oracle
+    is tested separately), and sampled outputs against the oracle."""
+    from x3_conv2d_epilogue_amd.synthetic import WORKLOADS, make_inputs
+    wl = WORKLOADS[name]
+    say("generating", wl.about)
+    d = make_inputs(wl)
+    g = {k: v.to(DEV) for k, v in d.items()}
+    xc = g["x"].contiguous(memory_format=torch.channels_last)
+    n = {k: v.numpy() for k, v in d.items() if k != "x"}
+    x = d["x"].numpy()
+    if name == "min_tanh2":
+        a, b = (x3.conv3x3_min_tanh2(xx, g["weight"], g["bias"]) for xx in (g["x"], xc))
+    elif name == "scale_min":
+        a, b = (x3.conv3x3_scale_min(xx, g["weight"], g["bias"], 2.0) for xx in (g["x"], xc))
+    elif name == "mul_lrelu_gelu":
+        a, b = (x3.conv3x3_mul_lrelu_gelu(xx, g["weight"], g["bias"], g["multiplier"], 0.01)
+                for xx in (g["x"], xc))
+    else:
+        p = wl.params
+        a, b = (x3.conv3x3_gn_scale_pool_clamp(xx, g["weight"], g["bias"], g["gamma"], g["beta"],
+                                               g["scale"], p["groups"], p["eps"], p["pool_k"],
+                                               -1e3, 1e3) for xx in (g["x"], xc))
+    torch.cuda.synchronize()
+    assert a.shape == b.shape
+    diff = (a - b).abs().max().item()
+    say(f"  {name}: NHWC vs NCHW max_abs_diff={diff:.3e}")
+    assert diff <= 2e-5, diff
+    if name == "gn_pool":
+        sub = {k: (v[:1] if k == "x" else v) for k, v in d.items()}
+        s = {k: v.numpy() for k, v in sub.items()}
+        p = wl.params
+        ref = oracle.gn_scale_pool_clamp(s["x"], s["weight"], s["bias"], s["gamma"], s["beta"],
+                                         s["scale"], p["groups"], p["eps"], p["pool_k"], -1e3, 1e3)
+        close(b[:1], ref, "gn sample 0 (NHWC)")
+        return
+    pix = _pixels(wl.B, wl.Ho, wl.Wo, 3000, 11)
+    got = b.detach().cpu()
+    if name == "mul_lrelu_gelu":
+        co = np.random.default_rng(12).integers(0, wl.Cout, pix.shape[0])
+        el = np.stack([pix[:, 0], co, pix[:, 1], pix[:, 2]], 1)
+        ref = oracle.mul_lrelu_gelu_at(x, n["weight"], n["bias"], n["multiplier"], el, 0.01)
+        sel = got[el[:, 0], el[:, 1], el[:, 2], el[:, 3]]
+    else:
+        ref = (oracle.min_tanh2_at(x, n["weight"], n["bias"], pix) if name == "min_tanh2"
+               else oracle.scale_min_at(x, n["weight"], n["bias"], pix, 2.0))
+        sel = got[pix[:, 0], 0, pix[:, 1], pix[:, 2]]
+    close(sel, ref, f"{name} sampled (NHWC)")
