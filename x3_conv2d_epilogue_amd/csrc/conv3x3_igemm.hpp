@@ -867,11 +867,18 @@ __global__ void __launch_bounds__(G::NTHR)
           sv[2 * gi + 1] = s2;
         }
       };
-      // (uniform) whole wave tiles need no masks
-      if (nrow_ok == G::NW && ncol_ok == 32)
+      // (uniform) whole wave tiles need no masks; with all rows valid, a
+      // lane's column is wholly valid or not, so its sums are dropped after
+      // the fact (16 selects instead of one per accumulator element)
+      if (nrow_ok == G::NW) {
         lane_sums(std::false_type{});
-      else
+        if (ncol_ok != 32) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) sv[k] = col_ok ? sv[k] : 0.0f;
+        }
+      } else {
         lane_sums(std::true_type{});
+      }
       // Sums over the 32 lanes of a half by a halving exchange: in each
       // step a lane keeps the half of its values selected by one lane bit,
       // adds the partner's copy of that half and hands over the other
