@@ -794,15 +794,19 @@ __global__ void __launch_bounds__(G::NTHR)
       uint32_t pixb[G::NW];
 #pragma unroll
       for (int j = 0; j < G::NW; ++j) pixb[j] = drop[j] ? drop[j] : pix_off[j] << 2;
+      // (the per-lane part of the channel's plane offset once; the rest is
+      // a constant times HoWo, a scalar product)
+      const uint32_t co_lane = (uint32_t)(co0 + 4 * h) * (uint32_t)HoWo;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int co = co0 + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+          const int cu = mt * 32 + 8 * (i >> 2) + (i & 3);
+          const int co = co0 + 4 * h + cu;
           const float mv = s_par[co];
           const uint32_t co_off =
               G::NHWC ? (uint32_t)co | ((uint32_t)(co >= a.Cout) << 31)
-                      : (uint32_t)co * HoWo;
+                      : co_lane + (uint32_t)cu * (uint32_t)HoWo;
 #pragma unroll
           for (int j = 0; j < G::NW; ++j) {
             const float y = op(acc[mt][j][i], mv);
