@@ -161,7 +161,8 @@ x3_status x3_epi_min_tanh2_f32(const float* y, float* out, int B, int C, int H,
 x3_status x3_epi_scale_min_f32(const float* y, float scale, float* out, int B,
                                int C, int H, int W, void* stream);
 
-/* [P54]: out = gelu_erf(lrelu(y * mult[c], neg_slope)), elementwise;
+/* [P54]: out = GELU(LeakyReLU(y * mult[c], neg_slope)), GELU in its exact
+ * (erf) form, elementwise;
  * mult [C]; out [B][C][H][W], may be y. */
 x3_status x3_epi_mul_lrelu_gelu_f32(const float* y, const float* mult,
                                     float neg_slope, float* out, int B, int C,
@@ -183,8 +184,11 @@ size_t x3_epi_gn_workspace_bytes(int B, int C);
  * H, W >= pool_k (else X3_ESHAPE); eps > 0, finite lo <= hi (else
  * X3_EINVAL).  workspace: at least x3_epi_gn_workspace_bytes(B, C) bytes,
  * 16-byte aligned, caller-owned, overwritten (else X3_EWORKSPACE /
- * X3_EINVAL).  Two kernels: per-plane statistics + window extrema (parked
- * in out), then the per-group finalize. */
+ * X3_EINVAL).  With pool_k == 4, W even, y 8-byte aligned, C / groups <= 64
+ * and a group's pooled block (C / groups * Ph * Pw floats) within 48 KB,
+ * one kernel per (sample, group) does everything and the workspace is not
+ * touched; otherwise two kernels: per-plane statistics + window extrema
+ * (parked in out), then the per-group finalize. */
 x3_status x3_epi_gn_scale_pool_clamp_f32(const float* y, const float* gamma,
                                          const float* beta, const float* scale,
                                          int groups, float eps, int pool_k,
