@@ -1,0 +1,43 @@
+"""The benchmark's command-line contract, on the CPU: it runs on exactly
+one GPU and says so for any other count, and its traffic figures are only
+reported for the kernel sources they were measured on."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "exactly one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_figures_follow_the_kernel_sources(tmp_path, monkeypatch):
+    import bench
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    d = json.load(open(p))
+    e = bench.load_traffic("min_tanh2")
+    if d.get("kernel_source_sha256") == bench.kernel_source_hash():
+        assert e is not None and e["bytes_per_launch"] > e["algorithmic_bytes"] * 0.9
+    else:
+        assert e is None
+    # a record taken on other sources is not reported
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
+    assert bench.load_traffic("min_tanh2") is None
+
+
+def test_algorithmic_counts_of_the_headline_workload():
+    import bench
+    from x3_conv2d_epilogue_amd.synthetic import WORKLOADS
+    wl = WORKLOADS["min_tanh2"]
+    # 2 * B * Cout * Ho * Wo * Cin * 9
+    assert wl.conv_flops() == 2 * 128 * 64 * 254 * 254 * 16 * 9 == 152_212_340_736
+    # x once + weights + bias + output, fp32
+    assert bench.algorithmic_bytes(wl) == 4 * (128 * 16 * 256 * 256 + 64 * 16 * 9 + 64
+                                               + 128 * 254 * 254)
