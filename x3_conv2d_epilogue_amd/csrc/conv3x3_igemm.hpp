@@ -764,26 +764,25 @@ __global__ void __launch_bounds__(G::NTHR)
       if (G::NHWC && (a.flags & kOutVec4)) {
         // NHWC with 16-byte stores: accumulator elements 4q..4q+3 are 4
         // consecutive channels of one pixel (a multiple of 4, so with
-        // Cout % 4 == 0 the 4 are real or padded together)
+        // Cout % 4 == 0 the 4 are real or padded together).  Pixel row by
+        // pixel row: the 2*MT*4 stores of a row complete its pixels' lines
+        // back to back (2.4 % faster than channel group by channel group).
+#pragma unroll
+        for (int j = 0; j < G::NW; ++j)
 #pragma unroll
         for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int co = co0 + mt * 32 + 8 * q + 4 * h;
             const uint32_t pad = (uint32_t)(co >= a.Cout) << 31;
-            float mv[4];
+            const f32x4 mv = *reinterpret_cast<const f32x4*>(&s_par[co]);
+            u32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mv[e] = s_par[co + e];
-#pragma unroll
-            for (int j = 0; j < G::NW; ++j) {
-              u32x4 v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                v[e] = __builtin_bit_cast(uint32_t, op(acc[mt][j][4 * q + e], mv[e]));
-              const uint32_t off =
-                  ((pix_off[j] + (uint32_t)co) << 2) | drop[j] | pad;
-              __builtin_amdgcn_raw_buffer_store_b128(v, o_rsrc, off, 0, 0);
-            }
+            for (int e = 0; e < 4; ++e)
+              v[e] = __builtin_bit_cast(uint32_t, op(acc[mt][j][4 * q + e], mv[e]));
+            const uint32_t off =
+                ((pix_off[j] + (uint32_t)co) << 2) | drop[j] | pad;
+            __builtin_amdgcn_raw_buffer_store_b128(v, o_rsrc, off, 0, 0);
           }
         return;
       }
