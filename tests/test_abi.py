@@ -171,6 +171,11 @@ def test_gn_validation(lib):
     assert call(ws=fake(0x60000004)) == EINVAL  # misaligned workspace
     assert call(out=X) == EINVAL
     assert call(ws=O) == EINVAL  # workspace overlaps out
+    # the workspace overlapping any parameter vector is refused too (the
+    # kernels write partials while other workgroups still read them)
+    for name, ptr in (("b", B_), ("g", M), ("be", fake(0x51000000)), ("sc", fake(0x52000000))):
+        assert call(ws=fake(ptr.value - 16)) == EINVAL, name
+        assert b"overlaps" in lib.x3_last_error()
     assert call(B=0, x=None, out=None) == OK
 
 
@@ -268,3 +273,4 @@ def test_nhwc_entry_validation(lib):
              1 << 20, 2, 8, 34, 34, 64, s) == EUNSUP
     assert g(X, W_, B_, M, fake(0x51000000), fake(0x52000000), 16, 1e-5, 4, 0.0, 1.0, O, ws,
              16, 2, 8, 34, 34, 64, s) == EWS
+

@@ -35,6 +35,14 @@ def test_traffic_figures_follow_the_kernel_sources(tmp_path, monkeypatch):
 def test_algorithmic_counts_of_the_headline_workload():
     import bench
     from x3_conv2d_epilogue_amd.synthetic import WORKLOADS
+    # the headline is the largest workload: 64->128 on [64,64,256,256]
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--workload", default="scale_min")' in src
+    big = max(WORKLOADS.values(), key=lambda w: w.conv_flops())
+    assert big.name == "scale_min"
+    assert big.conv_flops() == 2 * 64 * 128 * 254 * 254 * 64 * 9 == 608_849_362_944
+    assert bench.algorithmic_bytes(big) == 4 * (64 * 64 * 256 * 256 + 128 * 64 * 9 + 128
+                                                + 64 * 254 * 254)
     wl = WORKLOADS["min_tanh2"]
     # 2 * B * Cout * Ho * Wo * Cin * 9
     assert wl.conv_flops() == 2 * 128 * 64 * 254 * 254 * 16 * 9 == 152_212_340_736

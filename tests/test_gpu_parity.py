@@ -377,64 +377,79 @@ def test_workload_tiny_full():
     assert_close(run_op("min_tanh2", d), run_oracle("min_tanh2", d), what="tiny")
 
 
-def test_workload_min_tanh2_sampled():
+def _whole(got, ref, what):
+    """Element-by-element comparison of a full-size output, one sample at a
+    time (no full-size float64 temporaries); prints the whole-tensor
+    max-abs error."""
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    mx, at = 0.0, None
+    for n in range(got.shape[0]):
+        e = np.abs(got[n].astype(np.float64) - ref[n])
+        m = float(e.max())
+        if m > mx:
+            mx, at = m, (n,) + np.unravel_index(int(np.argmax(e)), e.shape)
+    say(f"  {what}: whole-tensor max_abs_err={mx:.3e} at {at} over {got.size} outputs")
+    assert np.all(np.isfinite(got)), what
+    assert mx <= TOL, f"{what}: max-abs {mx:.3e} > {TOL} at {at}"
+
+
+def test_workload_min_tanh2_full():
     wl = WORKLOADS["min_tanh2"]
     say("generating", wl.about)
     d = make_inputs(wl)
     got = run_op("min_tanh2", d)
     assert got.shape == (wl.B, 1, wl.Ho, wl.Wo)
-    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 20000, 1)
+    _whole(got, oracle.min_tanh2(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy()),
+           "min_tanh2 [128,16,256,256]")
+    # and the separately written single-output form of the oracle, on edge
+    # and random pixels
+    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 2000, 1)
     ref = oracle.min_tanh2_at(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(), pix)
     assert_close(got[pix[:, 0], 0, pix[:, 1], pix[:, 2]], ref, what="min_tanh2 sampled")
-    # one whole sample, every pixel
-    full0 = oracle.min_tanh2(d["x"][:1].numpy(), d["weight"].numpy(), d["bias"].numpy())
-    assert_close(got[:1], full0, what="min_tanh2 sample 0")
 
 
-def test_workload_mul_lrelu_gelu_sampled():
+def test_workload_mul_lrelu_gelu_full():
     wl = WORKLOADS["mul_lrelu_gelu"]
     say("generating", wl.about)
     d = make_inputs(wl)
     got = run_op("mul_lrelu_gelu", d)
     assert got.shape == (wl.B, wl.Cout, wl.Ho, wl.Wo)
-    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 40000, 2)
+    n = {k: v.numpy() for k, v in d.items()}
+    _whole(got, oracle.mul_lrelu_gelu(n["x"], n["weight"], n["bias"], n["multiplier"], 0.01),
+           "mul_lrelu_gelu [64,64,256,256]")
+    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 4000, 2)
     co = np.random.default_rng(3).integers(0, wl.Cout, pix.shape[0])
     el = np.stack([pix[:, 0], co, pix[:, 1], pix[:, 2]], 1)
-    ref = oracle.mul_lrelu_gelu_at(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(),
-                                   d["multiplier"].numpy(), el, 0.01)
+    ref = oracle.mul_lrelu_gelu_at(n["x"], n["weight"], n["bias"], n["multiplier"], el, 0.01)
     assert_close(got[el[:, 0], el[:, 1], el[:, 2], el[:, 3]], ref, what="mul_lrelu_gelu sampled")
-    assert np.all(np.isfinite(got))
 
 
-def test_workload_scale_min_sampled():
+def test_workload_scale_min_full():
     wl = WORKLOADS["scale_min"]
     say("generating", wl.about)
     d = make_inputs(wl)
     got = run_op("scale_min", d, scale=2.0)
     assert got.shape == (wl.B, 1, wl.Ho, wl.Wo)
-    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 12000, 4)
-    ref = oracle.scale_min_at(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(), pix, 2.0)
+    n = {k: v.numpy() for k, v in d.items()}
+    _whole(got, oracle.scale_min(n["x"], n["weight"], n["bias"], 2.0),
+           "scale_min [64,64,256,256]")
+    pix = _sample_pixels(wl.B, wl.Ho, wl.Wo, 2000, 4)
+    ref = oracle.scale_min_at(n["x"], n["weight"], n["bias"], pix, 2.0)
     assert_close(got[pix[:, 0], 0, pix[:, 1], pix[:, 2]], ref, what="scale_min sampled")
 
 
-def test_workload_gn_pool_full_samples():
+def test_workload_gn_pool_full():
+    """All 128 samples, with the [0, 1] clamp of the workload (most outputs
+    saturate at 1) and with a widened clamp that exposes every value."""
     wl = WORKLOADS["gn_pool"]
     say("generating", wl.about)
     d = make_inputs(wl)
-    got = run_op("gn_scale_pool_clamp", d)
-    assert got.shape == (wl.B, wl.Cout, 31, 31)
-    assert got.min() >= 0.0 and got.max() <= 1.0
-    for n in (0, 77, wl.B - 1):
-        sub = {k: (v[n:n + 1] if k == "x" else v) for k, v in d.items()}
-        ref = run_oracle("gn_scale_pool_clamp", sub)
-        assert_close(got[n:n + 1], ref, what=f"gn sample {n}")
-    # widened clamp: most outputs saturate at 1 in [0, 1]; check the values
-    wide = dict(lo=-1e3, hi=1e3)
-    got_w = run_op("gn_scale_pool_clamp", d, **wide)
-    for n in (0, 64):
-        sub = {k: (v[n:n + 1] if k == "x" else v) for k, v in d.items()}
-        assert_close(got_w[n:n + 1], run_oracle("gn_scale_pool_clamp", sub, **wide),
-                     what=f"gn wide sample {n}")
+    for lo, hi in ((0.0, 1.0), (-1e3, 1e3)):
+        got = run_op("gn_scale_pool_clamp", d, lo=lo, hi=hi)
+        assert got.shape == (wl.B, wl.Cout, 31, 31)
+        assert got.min() >= lo and got.max() <= hi
+        _whole(got, run_oracle("gn_scale_pool_clamp", d, lo=lo, hi=hi),
+               f"gn_pool [128,8,128,128] clamp [{lo},{hi}]")
 
 
 def test_misaligned_buffers_take_the_scalar_paths():

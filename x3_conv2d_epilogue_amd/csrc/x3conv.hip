@@ -347,7 +347,9 @@ x3_status gn_entry(const float* x, const float* w, const float* b,
       overlaps(out, ob, beta, cb) || overlaps(out, ob, scale, cb) ||
       overlaps(out, ob, workspace, need) ||
       overlaps(workspace, need, x, s.x_bytes()) ||
-      overlaps(workspace, need, w, s.w_bytes()))
+      overlaps(workspace, need, w, s.w_bytes()) ||
+      overlaps(workspace, need, b, cb) || overlaps(workspace, need, gamma, cb) ||
+      overlaps(workspace, need, beta, cb) || overlaps(workspace, need, scale, cb))
     return fail(X3_EINVAL, "out or workspace overlaps another buffer");
 
   hipStream_t st = (hipStream_t)stream;
@@ -566,7 +568,9 @@ X3_API x3_status x3_epi_gn_scale_pool_clamp_f32(
   const size_t yb = (size_t)B * C * H * W * 4;
   if (overlaps(out, ob, y, yb) || overlaps(out, ob, gamma, cb) ||
       overlaps(out, ob, beta, cb) || overlaps(out, ob, scale, cb) ||
-      overlaps(out, ob, workspace, need) || overlaps(workspace, need, y, yb))
+      overlaps(out, ob, workspace, need) || overlaps(workspace, need, y, yb) ||
+      overlaps(workspace, need, gamma, cb) || overlaps(workspace, need, beta, cb) ||
+      overlaps(workspace, need, scale, cb))
     return fail(X3_EINVAL, "out or workspace overlaps another buffer");
   x3::GnPlaneArgs g{};
   g.y = y;
