@@ -142,6 +142,29 @@ x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
     float lo, float hi, float* out, void* workspace, size_t workspace_bytes,
     int B, int Cin, int H, int W, int Cout, void* stream);
 
+/* Size of the static device scratch of
+ * x3_conv3x3_gn_scale_pool_clamp_noalloc_f32 (per GPU). */
+#define X3_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc:
+ * x3_conv3x3_gn_scale_pool_clamp_f32 (NCHW) without the workspace
+ * arguments.  Same operation, arguments, layouts and errors otherwise.  The
+ * partial statistics go to a static device array of
+ * X3_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; a shape whose workspace
+ * (x3_conv3x3_gn_workspace_bytes) exceeds it returns X3_EWORKSPACE.  The
+ * call allocates and frees nothing.  The scratch of a GPU is the one of the
+ * device current on the calling thread, so `stream` must belong to that
+ * device.  All calls on one GPU share its scratch: calls that can overlap
+ * in time on one GPU (streams not ordered with each other) race and must
+ * not be issued. */
+x3_status x3_conv3x3_gn_scale_pool_clamp_noalloc_f32(
+    const float* x, const float* w, const float* b, const float* gamma,
+    const float* beta, const float* scale, int groups, float eps, int pool_k,
+    float lo, float hi, float* out, int B, int Cin, int H, int W, int Cout,
+    void* stream);
+
 /* ------------------------------------------------------------------------
  * Standalone epilogues over a stored conv output y [B][C][H][W] (NCHW,
  * fp32, device memory owned by the caller).  Each is one HBM-bound kernel;

@@ -274,3 +274,31 @@ def test_nhwc_entry_validation(lib):
     assert g(X, W_, B_, M, fake(0x51000000), fake(0x52000000), 16, 1e-5, 4, 0.0, 1.0, O, ws,
              16, 2, 8, 34, 34, 64, s) == EWS
 
+
+def test_noalloc_gn_validation(lib):
+    """The allocation-free GroupNorm entry point validates like the
+    workspace form and refuses a shape whose partial statistics exceed its
+    static scratch, all before touching the device."""
+    f = lib.x3_conv3x3_gn_scale_pool_clamp_noalloc_f32
+    s = P(0)
+    BE, SC = fake(0x51000000), fake(0x52000000)
+
+    def call(**kw):
+        a = dict(x=X, w=W_, b=B_, g=M, be=BE, sc=SC, groups=16, eps=1e-5, k=4, lo=0.0, hi=1.0,
+                 out=O, B=2, Cin=8, H=34, W=34, Cout=64)
+        a.update(kw)
+        return f(a["x"], a["w"], a["b"], a["g"], a["be"], a["sc"], a["groups"], a["eps"], a["k"],
+                 a["lo"], a["hi"], a["out"], a["B"], a["Cin"], a["H"], a["W"], a["Cout"], s)
+
+    assert call(groups=0) == EINVAL
+    assert call(groups=5) == ESHAPE
+    assert call(eps=0.0) == EINVAL
+    assert call(lo=2.0) == EINVAL
+    assert call(g=None) == EINVAL
+    assert call(out=X) == EINVAL
+    assert call(B=0, x=None, out=None) == OK
+    # 1024 samples of [8,128,128] -> 64 channels: 1024*16*128 partials of
+    # 16 B = 32 MiB > the 16 MiB scratch
+    assert lib.x3_conv3x3_gn_workspace_bytes(1024, 8, 128, 128, 64, 16, 4) > x3.NOALLOC_SCRATCH_BYTES
+    assert call(B=1024, H=128, W=128) == EWS
+    assert b"static scratch" in lib.x3_last_error()

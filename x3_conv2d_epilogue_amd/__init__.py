@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "conv3x3_min_tanh2", "conv3x3_mul_lrelu_gelu", "conv3x3_mul_lrelu_gelu_tanh",
     "conv3x3_scale_min", "conv3x3_gn_scale_pool_clamp", "gn_workspace_bytes",
+    "conv3x3_gn_scale_pool_clamp_noalloc", "NOALLOC_SCRATCH_BYTES",
     "conv3x3_bias", "epi_min_tanh2", "epi_scale_min", "epi_mul_lrelu_gelu",
     "epi_mul_lrelu_gelu_tanh", "epi_gn_scale_pool_clamp",
     "library_path", "version", "X3Error", "load_library", "EXPORTED_SYMBOLS",
@@ -33,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "x3_conv3x3_min_tanh2_f32", "x3_conv3x3_mul_lrelu_gelu_f32",
     "x3_conv3x3_mul_lrelu_gelu_tanh_f32", "x3_conv3x3_bias_f32",
     "x3_conv3x3_scale_min_f32", "x3_conv3x3_gn_workspace_bytes",
-    "x3_conv3x3_gn_scale_pool_clamp_f32",
+    "x3_conv3x3_gn_scale_pool_clamp_f32", "x3_conv3x3_gn_scale_pool_clamp_noalloc_f32",
     "x3_conv3x3_min_tanh2_nhwc_f32", "x3_conv3x3_mul_lrelu_gelu_nhwc_f32",
     "x3_conv3x3_scale_min_nhwc_f32", "x3_conv3x3_gn_nhwc_workspace_bytes",
     "x3_conv3x3_gn_scale_pool_clamp_nhwc_f32",
@@ -96,6 +97,8 @@ def load_library():
     lib.x3_conv3x3_gn_workspace_bytes.restype = sz
     lib.x3_conv3x3_gn_scale_pool_clamp_f32.argtypes = [
         vp, vp, vp, vp, vp, vp, i, f, i, f, f, vp, vp, sz, i, i, i, i, i, vp]
+    lib.x3_conv3x3_gn_scale_pool_clamp_noalloc_f32.argtypes = [
+        vp, vp, vp, vp, vp, vp, i, f, i, f, f, vp, i, i, i, i, i, vp]
     for name in EXPORTED_SYMBOLS:
         if name.endswith("_f32"):
             getattr(lib, name).restype = i
@@ -283,6 +286,35 @@ def conv3x3_gn_scale_pool_clamp(x, weight, bias, gamma, beta, scale, groups=16,
         _ptr(x), _ptr(w), _ptr(b), _ptr(g), _ptr(be), _ptr(s), int(groups), float(eps), k,
         float(lo), float(hi), _ptr(out), _ptr(workspace), ws_bytes, B, Cin, H, W, Cout,
         _stream(x.device)))
+    return out
+
+
+# Size of the library's static device scratch (X3_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def conv3x3_gn_scale_pool_clamp_noalloc(x, weight, bias, gamma, beta, scale, groups=16,
+                                        eps=1e-5, pool_k=4, lo=0.0, hi=1.0,
+                                        out=None) -> torch.Tensor:
+    """conv3x3_gn_scale_pool_clamp through the allocation-free entry point:
+    the partial statistics live in the library's static device scratch, so
+    the library allocates nothing (pass `out` to allocate nothing at all).
+    NCHW x only; calls on one GPU must not overlap in time."""
+    lib = load_library()
+    x, w, b, B, Cin, H, W, Cout = _conv_inputs(x, weight, bias)
+    if is_nhwc(x):
+        raise ValueError("the allocation-free GroupNorm entry point takes NCHW x")
+    g = _vec(gamma, "gamma", Cout)
+    be = _vec(beta, "beta", Cout)
+    s = _vec(scale, "scale", Cout)
+    k = int(pool_k)
+    Ph = (H - 2 - k) // k + 1 if (k > 0 and H - 2 >= k) else 0
+    Pw = (W - 2 - k) // k + 1 if (k > 0 and W - 2 >= k) else 0
+    out = _out(out, (B, Cout, Ph, Pw), x)
+    _check("x3_conv3x3_gn_scale_pool_clamp_noalloc_f32",
+           lib.x3_conv3x3_gn_scale_pool_clamp_noalloc_f32(
+               _ptr(x), _ptr(w), _ptr(b), _ptr(g), _ptr(be), _ptr(s), int(groups), float(eps),
+               k, float(lo), float(hi), _ptr(out), B, Cin, H, W, Cout, _stream(x.device)))
     return out
 
 

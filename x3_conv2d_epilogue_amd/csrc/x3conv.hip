@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "dispatch.hpp"
 
@@ -304,6 +305,52 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
 }
 }  // namespace
 
+// ----------------------------------------------------------------------------
+// Static device scratch of the allocation-free GroupNorm entry point, for
+// callers that cannot allocate device memory.  It holds the partial
+// statistics that the caller's workspace holds otherwise.  Every GPU the
+// library runs on holds its own copy of `scratch`, at its own address, until
+// the process ends.  In host code the array's name is only a host-side
+// handle: the device address of the current GPU's copy is looked up once per
+// device with hipGetSymbolAddress and kept, and only that address is ever
+// handed to a kernel.  Calls on one GPU share the array, so calls that
+// overlap in time on one GPU (unordered streams) race.  No kernel needs the
+// array cleared: every partial slot a call reads is written earlier in the
+// same call.
+namespace {
+constexpr size_t kScratchBytes = X3_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's scratch (nullptr and an error status
+// in `rc` on failure).
+void* scratch_address(x3_status& rc) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    rc = fail(X3_EHIP, "no usable current device for the static scratch (%s)",
+              e != hipSuccess ? hipGetErrorString(e) : "device id out of range");
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    rc = fail(X3_EHIP, "hipGetSymbolAddress(scratch) failed: %s",
+              hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+}  // namespace
+
 namespace {
 size_t gn_workspace_query(int B, int Cin, int H, int W, int Cout, int groups,
                           int pool_k, bool nhwc) {
@@ -320,7 +367,8 @@ x3_status gn_entry(const float* x, const float* w, const float* b,
                    const float* gamma, const float* beta, const float* scale,
                    int groups, float eps, int pool_k, float lo, float hi,
                    float* out, void* workspace, size_t workspace_bytes, int B,
-                   int Cin, int H, int W, int Cout, void* stream, bool nhwc) {
+                   int Cin, int H, int W, int Cout, void* stream, bool nhwc,
+                   bool use_scratch = false) {
   g_err[0] = '\0';
   Shape s;
   x3_status rc = check_gn(B, Cin, H, W, Cout, groups, pool_k, nhwc, s);
@@ -334,11 +382,21 @@ x3_status gn_entry(const float* x, const float* w, const float* b,
     return fail(X3_EINVAL, "clamp bounds must be finite with lo <= hi");
   if (B == 0) return X3_OK;
   const size_t need = gn_workspace(s, groups, pool_k, nhwc);
-  if (!workspace || workspace_bytes < need)
-    return fail(X3_EWORKSPACE, "workspace of %zu bytes needed, got %zu", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (((uintptr_t)workspace & 15u) != 0)
-    return fail(X3_EINVAL, "workspace must be 16-byte aligned");
+  if (use_scratch) {
+    // the allocation-free entry point: the library's static scratch (its
+    // address is looked up once every check has passed)
+    if (need > kScratchBytes)
+      return fail(X3_EWORKSPACE,
+                  "this shape needs %zu bytes of workspace; the static scratch "
+                  "of the allocation-free entry point holds %zu",
+                  need, kScratchBytes);
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(X3_EWORKSPACE, "workspace of %zu bytes needed, got %zu", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace & 15u) != 0)
+      return fail(X3_EINVAL, "workspace must be 16-byte aligned");
+  }
   const int Ph = (s.Ho - pool_k) / pool_k + 1, Pw = (s.Wo - pool_k) / pool_k + 1;
   const size_t ob = (size_t)B * Cout * Ph * Pw * 4;
   const size_t cb = s.c_bytes();
@@ -351,6 +409,11 @@ x3_status gn_entry(const float* x, const float* w, const float* b,
       overlaps(workspace, need, b, cb) || overlaps(workspace, need, gamma, cb) ||
       overlaps(workspace, need, beta, cb) || overlaps(workspace, need, scale, cb))
     return fail(X3_EINVAL, "out or workspace overlaps another buffer");
+  if (use_scratch) {
+    workspace = scratch_address(rc);
+    if (!workspace) return rc;
+    workspace_bytes = kScratchBytes;
+  }
 
   hipStream_t st = (hipStream_t)stream;
   if (pool_k != 4) {
@@ -427,6 +490,15 @@ X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
   return gn_entry(x, w, b, gamma, beta, scale, groups, eps, pool_k, lo, hi,
                   out, workspace, workspace_bytes, B, Cin, H, W, Cout, stream,
                   false);
+}
+
+X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_noalloc_f32(
+    const float* x, const float* w, const float* b, const float* gamma,
+    const float* beta, const float* scale, int groups, float eps, int pool_k,
+    float lo, float hi, float* out, int B, int Cin, int H, int W, int Cout,
+    void* stream) {
+  return gn_entry(x, w, b, gamma, beta, scale, groups, eps, pool_k, lo, hi,
+                  out, nullptr, 0, B, Cin, H, W, Cout, stream, false, true);
 }
 
 X3_API x3_status x3_conv3x3_gn_scale_pool_clamp_nhwc_f32(
