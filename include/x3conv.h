@@ -128,12 +128,12 @@ size_t x3_conv3x3_gn_workspace_bytes(int B, int Cin, int H, int W, int Cout,
  * bytes, 16-byte aligned, owned by the caller, contents need not be
  * initialized; it is overwritten, and two calls sharing one workspace must
  * be ordered on one stream.  Two kernels are enqueued on `stream`.  With
- * pool_k == 4 the conv kernel writes statistics partials (workspace) and
- * the window extrema (out), then a finalize normalizes out in place.  Any
- * other pool_k takes the split path: the conv output goes to the workspace
- * (B*Cout*Ho*Wo floats, then B*Cout 16-byte partials at the next 256-byte
- * boundary), then x3_epi_gn_scale_pool_clamp_f32's kernels run on it.
- * Supported: any groups dividing Cout (Cout <= 1024), any pool_k >= 1;
+ * pool_k in 1..16 the conv kernel writes statistics partials (workspace)
+ * and the window extrema (out), then a finalize normalizes out in place.
+ * A larger pool_k takes the split path: the conv output goes to the
+ * workspace (B*Cout*Ho*Wo floats, then B*Cout 16-byte partials at the next
+ * 256-byte boundary), then x3_epi_gn_scale_pool_clamp_f32's kernels run on
+ * it.  Supported: any groups dividing Cout (Cout <= 1024), any pool_k >= 1;
  * eps > 0 and finite lo <= hi (else X3_EINVAL); Ho, Wo >= pool_k (else
  * X3_ESHAPE). */
 x3_status x3_conv3x3_gn_scale_pool_clamp_f32(
@@ -229,7 +229,9 @@ x3_status x3_epi_gn_scale_pool_clamp_f32(const float* y, const float* gamma,
  * coalesced staging of its direct convolution (channels contiguous per
  * pixel).  It is the layout PyTorch's channels_last tensors hold.  Arguments,
  * limits and errors are those of the NCHW entry points, except that the
- * GroupNorm form supports pool_k == 4 only.
+ * GroupNorm form supports pool_k 1..16 (no split path), and windows other
+ * than 4 need Cin % 4 == 0 and 16-byte aligned x and w (else
+ * X3_EUNSUPPORTED).
  * ------------------------------------------------------------------------ */
 
 /* (a) on NHWC x; out [B][Ho][Wo] (the same bytes in either layout). */
@@ -256,7 +258,7 @@ x3_status x3_conv3x3_scale_min_nhwc_f32(const float* x, const float* w,
 size_t x3_conv3x3_gn_nhwc_workspace_bytes(int B, int Cin, int H, int W,
                                           int Cout, int groups, int pool_k);
 
-/* (d) on NHWC x; out [B][Ph][Pw][Cout]; pool_k == 4. */
+/* (d) on NHWC x; out [B][Ph][Pw][Cout]; pool_k 1..16. */
 x3_status x3_conv3x3_gn_scale_pool_clamp_nhwc_f32(
     const float* x, const float* w, const float* b, const float* gamma,
     const float* beta, const float* scale, int groups, float eps, int pool_k,

@@ -125,11 +125,24 @@ def test_gn_workspace_bytes(lib):
     assert f(2, 8, 128, 128, 64, 8, 4) == 2 * 8 * 8 * 128 * 16
     # one group of all 64 channels
     assert f(2, 8, 128, 128, 64, 1, 4) == 2 * 1 * 64 * 128 * 16
-    # other pool windows take the split path: the workspace holds the conv
+    # windows 1..16 other than 4 run fused too, on tiles of 16 x 64 outputs
+    # trimmed to whole windows (NCHW columns to a multiple of lcm(k, 4)),
+    # 8 waves.  k = 2: 16 x 64 tiles, 8 * 2 * 8 = 128 slots per group of 4
+    assert f(2, 8, 128, 128, 64, 16, 2) == 2 * 16 * 128 * 16
+    # k = 3: 15 x 60 tiles, 9 * 3 * 8 = 216 slots, partials per channel
+    # (4 per group) for windows of 3 and more
+    assert f(2, 8, 128, 128, 64, 16, 3) == 2 * 16 * 4 * 216 * 16
+    # k = 7: 14 x 56 tiles -> 9 * 3 * 8 = 216 slots
+    assert f(2, 8, 128, 128, 64, 16, 7) == 2 * 16 * 4 * 216 * 16
+    # k = 16: 16 x 64 tiles -> 128 slots
+    assert f(2, 8, 128, 128, 64, 16, 16) == 2 * 16 * 4 * 128 * 16
+    # k = 1 (no pooling): 128 slots per group of 4
+    assert f(2, 8, 128, 128, 64, 16, 1) == 2 * 16 * 128 * 16
+    # larger windows take the split path: the workspace holds the conv
     # output, [2, 64, 126, 126] floats, then 2 * 64 plane partials of 16 B at
     # the next 256-byte boundary
     y_bytes = (2 * 64 * 126 * 126 * 4 + 255) // 256 * 256
-    assert f(2, 8, 128, 128, 64, 16, 3) == y_bytes + 2 * 64 * 16
+    assert f(2, 8, 128, 128, 64, 16, 17) == y_bytes + 2 * 64 * 16
     assert f(2, 8, 128, 128, 64, 16, 0) == 0   # pool 0: invalid
     assert f(2, 8, 5, 5, 64, 16, 4) == 0       # 3x3 conv output < pool window
     assert f(2, 8, 128, 128, 1028, 257, 4) == 0  # Cout above 1024
@@ -156,7 +169,8 @@ def test_gn_validation(lib):
     assert call(groups=5) == ESHAPE
     assert call(H=5) == ESHAPE
     assert call(groups=8) == EWS  # supported; needs per-channel partials
-    assert call(k=2) == EWS   # split path: the workspace must hold the conv output
+    assert call(k=2) == EWS   # window 2: 16 partial slots per group, more than k=4's 8
+    assert call(k=20) == EWS  # split path: the workspace must hold the conv output
     assert call(Cout=1028, groups=257) == EUNSUP
     # Cout 128 is supported, but needs a workspace for 32 groups
     assert call(Cout=128, groups=32) == EWS
@@ -256,10 +270,12 @@ def test_nhwc_entry_validation(lib):
     assert lib.x3_conv3x3_mul_lrelu_gelu_nhwc_f32(X, W_, B_, None, 0.01, O, 2, 16, 32, 32, 64,
                                                   s) == EINVAL
     assert lib.x3_conv3x3_min_tanh2_nhwc_f32(None, W_, B_, None, 0, 16, 32, 32, 64, s) == OK
-    # the NHWC GroupNorm form compiles only 4x4 windows
+    # the NHWC GroupNorm form pools windows 1..16 (no split path)
     f = lib.x3_conv3x3_gn_nhwc_workspace_bytes
     assert f(2, 8, 34, 34, 64, 16, 4) > 0
-    assert f(2, 8, 34, 34, 64, 16, 3) == 0
+    # k = 3, NHWC: 15 x 63 tiles -> 3 * 1 * 8 = 24 slots, 4 per group
+    assert f(2, 8, 34, 34, 64, 16, 3) == 2 * 16 * 4 * 24 * 16
+    assert f(2, 8, 40, 40, 64, 16, 17) == 0
     # [2,8,34,34] -> 32x32, Cin <= 8 and Cout <= 64: resident-weight tiles
     # of 16 rows x 32 columns, 4 waves -> 2 * 1 * 4 = 8 slots
     assert f(2, 8, 34, 34, 64, 16, 4) == 2 * 16 * 8 * 16
@@ -269,8 +285,8 @@ def test_nhwc_entry_validation(lib):
     assert f(1, 8, 128, 128, 64, 16, 4) == 16 * 16 * 2 * 4 * 16
     g = lib.x3_conv3x3_gn_scale_pool_clamp_nhwc_f32
     ws = fake(0x60000000)
-    assert g(X, W_, B_, M, fake(0x51000000), fake(0x52000000), 16, 1e-5, 3, 0.0, 1.0, O, ws,
-             1 << 20, 2, 8, 34, 34, 64, s) == EUNSUP
+    assert g(X, W_, B_, M, fake(0x51000000), fake(0x52000000), 16, 1e-5, 17, 0.0, 1.0, O, ws,
+             1 << 20, 2, 8, 40, 40, 64, s) == EUNSUP
     assert g(X, W_, B_, M, fake(0x51000000), fake(0x52000000), 16, 1e-5, 4, 0.0, 1.0, O, ws,
              16, 2, 8, 34, 34, 64, s) == EWS
 

@@ -214,3 +214,34 @@ def test_nhwc_workloads_full_size(name):
                else oracle.scale_min_at(x, n["weight"], n["bias"], pix, 2.0))
         sel = got[pix[:, 0], 0, pix[:, 1], pix[:, 2]]
     close(sel, ref, f"{name} sampled (NHWC)")
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 7, 16])
+@pytest.mark.parametrize("case", [((2, 8, 26, 37), 64, 16), ((1, 16, 35, 131), 48, 6),
+                                  ((1, 4, 20, 80), 128, 32)])
+def test_nhwc_gn_pool_other_windows(k, case):
+    """Windows other than 4 with channels-last x and output (the 16-byte
+    channel-half staging: Cin % 4 == 0)."""
+    shape, Cout, groups = case
+    B, Cin, H, W = shape
+    if H - 2 < k or W - 2 < k:
+        pytest.skip("window larger than the conv output")
+    say(f"nhwc gn k={k} {shape} Cout={Cout} groups={groups}")
+    d = random_case("gn_scale_pool_clamp", B, Cin, H, W, Cout, seed=1900 + k + Cout)
+    d["gamma"][1::4] *= -1.0
+    g = dev_cl(d)
+    out = x3.conv3x3_gn_scale_pool_clamp(g["x"], g["weight"], g["bias"], g["gamma"], g["beta"],
+                                         g["scale"], groups, 1e-5, k, -50.0, 50.0)
+    assert Cout == 1 or out.is_contiguous(memory_format=torch.channels_last)
+    n = {k_: v.numpy() for k_, v in d.items()}
+    close(out, oracle.gn_scale_pool_clamp(n["x"], n["weight"], n["bias"], n["gamma"], n["beta"],
+                                          n["scale"], groups, 1e-5, k, -50.0, 50.0), f"gn k={k}")
+
+
+def test_nhwc_gn_pool_other_windows_need_cin_multiple_of_4():
+    d = random_case("gn_scale_pool_clamp", 1, 3, 22, 39, 64, seed=1950)
+    g = dev_cl(d)
+    with pytest.raises(x3.X3Error) as e:
+        x3.conv3x3_gn_scale_pool_clamp(g["x"], g["weight"], g["bias"], g["gamma"], g["beta"],
+                                       g["scale"], 16, 1e-5, 3, 0.0, 1.0)
+    assert e.value.status_name == "X3_EUNSUPPORTED"

@@ -511,3 +511,76 @@ def test_gn_pool_any_group_size_constant_channels():
     kw = dict(groups=8, lo=-100.0, hi=100.0)
     assert_close(run_op("gn_scale_pool_clamp", d, **kw),
                  run_oracle("gn_scale_pool_clamp", d, **kw), what="all ones, 8 per group")
+
+
+# ----------------------------------------------------------------------------
+# GroupNorm with pooling windows other than 4, fused: tiles of 16 x 64 conv
+# outputs trimmed to whole windows; windows 1 and 2 fold inside a
+# wavefront, windows 3..16 are merged across wavefronts in LDS.
+
+POOLK = [1, 2, 3, 5, 6, 7, 8, 12, 16]
+POOLK_CASES = [  # (Cout, groups, (B, Cin, H, W))
+    (64, 16, (2, 8, 26, 37)),     # groups of 4, resident weights, ragged
+    (48, 6, (1, 8, 40, 70)),      # 8 channels per group, one padded block
+    (128, 32, (2, 16, 35, 131)),  # two 64-channel blocks, two K chunks
+    (64, 8, (1, 12, 20, 258)),    # several column tiles, Cin % 8 != 0
+]
+
+
+@pytest.mark.parametrize("k", POOLK)
+@pytest.mark.parametrize("case", range(len(POOLK_CASES)))
+def test_gn_pool_other_windows_fused(k, case):
+    Cout, groups, shape = POOLK_CASES[case]
+    B, Cin, H, W = shape
+    if H - 2 < k or W - 2 < k:
+        pytest.skip("window larger than the conv output")
+    say(f"gn pool k={k} {shape} Cout={Cout} groups={groups}")
+    d = random_case("gn_scale_pool_clamp", B, Cin, H, W, Cout, seed=1600 + 7 * k + case)
+    d["gamma"][::3] *= -1.0
+    d["scale"][2::5] *= -1.0
+    kw = dict(groups=groups, pool_k=k, lo=-50.0, hi=50.0)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw),
+                 run_oracle("gn_scale_pool_clamp", d, **kw), what=f"k={k} case {case}")
+
+
+@pytest.mark.parametrize("k", [2, 3, 5])
+def test_gn_pool_other_windows_many_tiles(k):
+    """More tiles than workgroups: a workgroup reuses its window buffer for
+    tiles of other samples; all gamma*scale >= 0 (the direction-free
+    form) and the [0, 1] clamp of the workload."""
+    d = random_case("gn_scale_pool_clamp", 48, 8, 34, 70, 64, seed=1700 + k)
+    d["gamma"] = d["gamma"].abs()
+    d["scale"] = d["scale"].abs()
+    kw = dict(pool_k=k)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw),
+                 run_oracle("gn_scale_pool_clamp", d, **kw), what=f"k={k} many tiles")
+
+
+def test_gn_pool_other_windows_workload_shape():
+    """The GroupNorm workload's shape, [128,8,128,128] -> 64 channels, with
+    3x3 and 2x2 windows: whole-tensor comparison."""
+    wl = WORKLOADS["gn_pool"]
+    d = make_inputs(wl)
+    for k in (3, 2):
+        kw = dict(pool_k=k, lo=-1e3, hi=1e3)
+        got = run_op("gn_scale_pool_clamp", d, **kw)
+        P = (wl.Ho - k) // k + 1
+        assert got.shape == (wl.B, wl.Cout, P, P)
+        _whole(got, run_oracle("gn_scale_pool_clamp", d, **kw), f"gn_pool k={k}")
+
+
+@pytest.mark.parametrize("k", [3, 2])
+def test_gn_pool_other_windows_misaligned_x(k):
+    """x 4 bytes off 16-byte alignment: the 4-byte staging form."""
+    d = random_case("gn_scale_pool_clamp", 2, 8, 30, 44, 64, seed=1800 + k)
+    g = to_dev(d)
+    xb = torch.empty(g["x"].numel() + 1, device=DEV)
+    xb[1:].copy_(g["x"].reshape(-1))
+    xm = xb[1:].view_as(g["x"])
+    assert xm.data_ptr() % 16 == 4
+    out = x3.conv3x3_gn_scale_pool_clamp(xm, g["weight"], g["bias"], g["gamma"], g["beta"],
+                                         g["scale"], 16, 1e-5, k, -50.0, 50.0)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(),
+                 run_oracle("gn_scale_pool_clamp", d, pool_k=k, lo=-50.0, hi=50.0),
+                 what=f"misaligned k={k}")

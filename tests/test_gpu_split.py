@@ -187,13 +187,13 @@ def test_conv3x3_mul_lrelu_gelu_tanh(shape, Cout):
                                                  n["multiplier"], 0.01), what="gelu tanh")
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 17, 20])
 @pytest.mark.parametrize("cg", [(64, 16), (48, 6)])
 def test_fused_entry_other_pool_sizes(k, cg):
-    """x3_conv3x3_gn_scale_pool_clamp_f32 with windows other than 4: conv
-    output in the workspace, then the standalone GroupNorm kernel."""
+    """x3_conv3x3_gn_scale_pool_clamp_f32 with windows other than 4 (fused
+    window-k kernels; windows above 16 take the split path, below)."""
     Cout, groups = cg
-    B, Cin, H, W = 2, 8, 26, 37
+    B, Cin, H, W = 2, 8, 26, 37 + (20 if k > 16 else 0)
     say(f"fused gn entry k={k} Cout={Cout} groups={groups}")
     d = random_case("gn_scale_pool_clamp", B, Cin, H, W, Cout, seed=500 + k)
     g = {k_: v.to(DEV) for k_, v in d.items()}

@@ -73,7 +73,12 @@ enum Epilogue : int {
   EPI_GN_POOL_CH = 4,      // GroupNorm partials per channel (any group
                            // size) + pooling-window extrema
   EPI_STORE = 5,           // the conv output itself (split path)
-  EPI_MUL_LRELU_GELU_TANH = 6  // tanh-form GELU(LeakyReLU(y * mult[co]))
+  EPI_MUL_LRELU_GELU_TANH = 6,  // tanh-form GELU(LeakyReLU(y * mult[co]))
+  EPI_GN_POOLK = 7,        // GroupNorm partials per group of 4 channels +
+                           // extrema of pooling windows of size 1 or 2
+  EPI_GN_POOLK_CH = 8,     // per-channel partials + windows of size 1 or 2
+  EPI_GN_POOLKL = 9        // per-channel partials + windows of size 3..16,
+                           // combined across wavefronts in LDS
 };
 
 // Kernel arguments (plain values, passed by value).
@@ -97,12 +102,32 @@ struct ConvArgs {
   int groups;       // GroupNorm groups (EPI_GN_POOL*)
   int flags;        // kOutVec4: NHWC out takes 16-byte stores (Cout % 4
                     // == 0 and out 16-byte aligned)
+  int pk;           // pooling window (EPI_GN_POOLK*)
+  int thk, twk;     // output rows / columns a tile covers (set by the
+                    // launcher: TH x TWC, or for EPI_GN_POOLK* the largest
+                    // multiples of the window that fit, so that no window
+                    // crosses a tile)
 };
 
 constexpr int kOutVec4 = 1;
 
 // Largest Cout: per-channel constants of all channel blocks live in LDS.
 constexpr int kMaxCout = 1024;
+
+// Pooling windows other than 4x4 (EPI_GN_POOLK*): sizes 1 and 2 fold
+// inside a wavefront; sizes 3..16 are combined across the wavefronts of a
+// tile in LDS, where a tile of TH x TWC outputs holds at most (TH/3) x
+// (TWC/3) windows.  (Separate kernels: with all three forms, or with
+// group-of-4 partials next to the LDS window buffer, the kernel needs more
+// than the 256 registers of two waves per SIMD.)
+template <int EPI>
+constexpr bool gn_generic_k() {
+  return EPI == EPI_GN_POOLK || EPI == EPI_GN_POOLK_CH || EPI == EPI_GN_POOLKL;
+}
+template <int EPI>
+constexpr bool gn_epilogue() {
+  return EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH || gn_generic_k<EPI>();
+}
 
 // Compile-time geometry of one kernel configuration.
 template <int MT_, int CC_, int TH_, int NCT_, int NWAVE_, bool X4_,
@@ -378,8 +403,8 @@ __global__ void __launch_bounds__(G::NTHR)
     const int rt = (t / a.n_ct) % a.n_rt;
     Item it;
     it.n = t / (a.n_ct * a.n_rt);
-    it.r0 = rt * G::TH;
-    it.c0 = ct * G::TWC;
+    it.r0 = rt * a.thk;
+    it.c0 = ct * a.twk;
     it.ci0 = chunk * G::CC;
     it.co0 = cb * G::COUT;
     return it;
@@ -591,7 +616,7 @@ __global__ void __launch_bounds__(G::NTHR)
         pv = a.v0[co] * kGeluIn;  // (the folded form of mul_lrelu_gelu_erf)
       if constexpr (EPI == EPI_MUL_LRELU_GELU_TANH)
         pv = a.v0[co];
-      if constexpr (EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH)
+      if constexpr (gn_epilogue<EPI>())
         pv = ((a.v0[co] >= 0.0f) == (a.v2[co] >= 0.0f)) ? 1.0f : -1.0f;
     }
     s_bias[co] = bv;
@@ -603,8 +628,20 @@ __global__ void __launch_bounds__(G::NTHR)
   // (gamma*scale >= 0 throughout, the usual case); then the extrema need
   // no direction factor.
   bool all_max = false;
-  if constexpr (EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH)
+  if constexpr (gn_epilogue<EPI>())
     all_max = __builtin_amdgcn_readfirstlane(!__syncthreads_or(dir_neg)) != 0;
+  // Windows of any size (k >= 3) are combined across the wavefronts of a
+  // tile in this buffer, [channel of the block][window row][window column]
+  // of the tile, before they are stored; it starts (and is left) at -inf.
+  // A channel's windows take at most WINCH slots (k >= 3), its fixed stride.
+  constexpr int WINCH = (G::TH / 3) * (G::TWC / 3);
+  constexpr int WINBUF = EPI == EPI_GN_POOLKL ? G::COUT * WINCH : 1;
+  static_assert((G::LDS_DWORDS + 2 * kMaxCout + WINBUF) * 4 <= 160 * 1024,
+                "LDS budget exceeded");
+  __shared__ float s_win[WINBUF];
+  if constexpr (EPI == EPI_GN_POOLKL) {
+    for (int i = tid; i < WINBUF; i += G::NTHR) s_win[i] = -__builtin_inff();
+  }
 
   f32x16 acc[G::MT][G::NW];
   // running channel extremum of the min epilogues, per N-tile, carried from
@@ -621,7 +658,10 @@ __global__ void __launch_bounds__(G::NTHR)
   // the flush is unconditional.  (The GroupNorm epilogue stores at once:
   // parking its results raised the register count past the budget.)
   constexpr bool DEFER = EPI == EPI_MIN_TANH2 || EPI == EPI_SCALE_MIN;
-  constexpr bool IS_GN = EPI == EPI_GN_POOL || EPI == EPI_GN_POOL_CH;
+  constexpr bool IS_GN = gn_epilogue<EPI>();
+  // per-group partials (groups of 4 channels) or per-channel partials
+  constexpr bool GN_CH =
+      EPI == EPI_GN_POOL_CH || EPI == EPI_GN_POOLK_CH || EPI == EPI_GN_POOLKL;
   constexpr int NPEND = DEFER ? G::NW / 2 : 1;
   constexpr uint32_t DROP = 0x80000000u;
   uint32_t pend_v[NPEND], pend_off[NPEND];
@@ -643,7 +683,7 @@ __global__ void __launch_bounds__(G::NTHR)
   };
   auto part_rsrc = [&](int n) X3_INLINE {
     const int pps = a.n_rt * a.n_ct * G::NWAVE;
-    const int rows = EPI == EPI_GN_POOL_CH ? a.Cout : a.groups;
+    const int rows = GN_CH ? a.Cout : a.groups;
     return make_rsrc(a.part + (size_t)n * rows * pps, (uint32_t)(rows * pps * 16));
   };
   // Pin the parked values where the epilogue computed them: left free, the
@@ -674,8 +714,8 @@ __global__ void __launch_bounds__(G::NTHR)
     const int ct = t % a.n_ct;
     const int rt = (t / a.n_ct) % a.n_rt;
     const int n = t / (a.n_ct * a.n_rt);
-    const int r_base = rt * G::TH + wm.row0;           // output row of j = 0
-    const int c = ct * G::TWC + wm.strip * 32 + l32;   // output column
+    const int r_base = rt * a.thk + wm.row0;           // output row of j = 0
+    const int c = ct * a.twk + wm.strip * 32 + l32;    // output column
     const bool col_ok = c < a.Wo;
 
     if constexpr (EPI == EPI_MIN_TANH2 || EPI == EPI_SCALE_MIN) {
@@ -817,8 +857,8 @@ __global__ void __launch_bounds__(G::NTHR)
                 __builtin_bit_cast(uint32_t, y), o_rsrc, off, 0, 0);
           }
         }
-    } else {  // EPI_GN_POOL(_CH): requires NW == 4 and pool 4
-      static_assert(G::NW == 4, "pool needs 4 rows");
+    } else {  // the GroupNorm epilogues: wave tiles of 4 rows
+      static_assert(G::NW == 4, "GroupNorm epilogues need 4-row wave tiles");
       // Stores go through raw buffer resources over this sample's slice of
       // `part` and `out` (out_rsrc, part_rsrc); a store that must not happen
       // gets bit 31 set in its offset (past num_records, dropped by the
@@ -834,12 +874,15 @@ __global__ void __launch_bounds__(G::NTHR)
       // deviations are taken in one pass from a shift K, a conv value of
       // the same group (so |mean - K| is of the order of the spread):
       // S1 = sum(x - K), S2 = sum((x - K)^2), M2 = S2 - S1^2 / n.
-      int nrow_ok = a.Ho - r_base;
+      // valid rows: inside the image and inside the tile's thk rows (a
+      // prefix of the wave's rows); valid columns likewise
+      int nrow_ok = min(a.Ho - r_base, a.thk - wm.row0);
       nrow_ok = nrow_ok < 0 ? 0 : (nrow_ok > G::NW ? G::NW : nrow_ok);
-      int ncol_ok = a.Wo - (ct * G::TWC + wm.strip * 32);
+      int ncol_ok = min(a.Wo - (ct * a.twk + wm.strip * 32), a.twk - wm.strip * 32);
       ncol_ok = ncol_ok < 0 ? 0 : (ncol_ok > 32 ? 32 : ncol_ok);
+      const bool col_ok = l32 < ncol_ok;
       const int slot = (rt * a.n_ct + ct) * G::NWAVE + wave;
-      if constexpr (EPI == EPI_GN_POOL) {
+      if constexpr (!GN_CH) {
       static_assert(G::MT == 2, "8 groups per lane half");
       const float cnt = (float)(4 * nrow_ok * ncol_ok);
       const float inv_cnt = cnt > 0.0f ? 1.0f / cnt : 0.0f;
@@ -1005,70 +1048,196 @@ __global__ void __launch_bounds__(G::NTHR)
               __builtin_bit_cast(u32x4, v), p_rsrc, off, 0, 0);
         }
       }
+      if constexpr (!gn_generic_k<EPI>()) {
+        // (the statistics are complete: keep the window code from being
+      // interleaved with them, which would hold both phases' values at once)
+      __builtin_amdgcn_sched_barrier(0);
       // (2) 4x4 window extrema.  The wave's 4 N-tiles are 4 consecutive
-      // rows starting at a multiple of 4, and 4 consecutive lanes are 4
-      // consecutive columns starting at a multiple of 4, so a window is
-      // (4 rows in-lane) x (4 lanes of a quad).  Only the extremum that the
-      // monotone GroupNorm-affine-scale map sends to the window maximum is
-      // stored: the max where gamma*scale >= 0, else the min.  Both are
-      // taken as a maximum of sg*y, sg = +-1 the channel's direction (exact:
-      // negation is exact and min(y) = -max(-y)), so each value enters one
-      // max chain.  Across the quad a halving exchange on lane bits 0 and 1
-      // leaves channel 2*b0 + b1 of the 4-channel block in each lane.
-      const int py = (rt * G::TH + wm.row0) >> 2;
-      const int px = (ct * G::TWC + wm.strip * 32 + l32) >> 2;
-      const uint32_t win_off = (uint32_t)(py * a.Pw + px);
-      const uint32_t win_bad = (uint32_t)!(py < a.Ph && px < a.Pw) << 31;
-      const bool q0 = lane & 1, q1 = (lane >> 1) & 1;
-      const int e = 2 * q0 + q1;
-      // SG: per-channel direction factors; without (all_max) the chains
-      // take the raw values.  (one uniform branch around two compile-time
-      // forms)
-      auto extrema = [&](auto sgc) X3_INLINE {
-        constexpr bool SG = decltype(sgc)::value;
-#pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int cq = co0 + mt * 32 + 8 * q + 4 * h;  // first channel
-            f32x4 sg = {1.0f, 1.0f, 1.0f, 1.0f};
-            if constexpr (SG) sg = *reinterpret_cast<const f32x4*>(&s_par[cq]);
-            f32x4 t;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              float m = SG ? sg[e2] * acc[mt][0][4 * q + e2] : acc[mt][0][4 * q + e2];
-#pragma unroll
-              for (int j = 1; j < G::NW; ++j)
-                m = vmax(m, SG ? sg[e2] * acc[mt][j][4 * q + e2] : acc[mt][j][4 * q + e2]);
-              t[e2] = m;
+        // rows starting at a multiple of 4, and 4 consecutive lanes are 4
+        // consecutive columns starting at a multiple of 4, so a window is
+        // (4 rows in-lane) x (4 lanes of a quad).  Only the extremum that the
+        // monotone GroupNorm-affine-scale map sends to the window maximum is
+        // stored: the max where gamma*scale >= 0, else the min.  Both are
+        // taken as a maximum of sg*y, sg = +-1 the channel's direction (exact:
+        // negation is exact and min(y) = -max(-y)), so each value enters one
+        // max chain.  Across the quad a halving exchange on lane bits 0 and 1
+        // leaves channel 2*b0 + b1 of the 4-channel block in each lane.
+        const int py = r_base >> 2;
+        const int px = c >> 2;
+        const uint32_t win_off = (uint32_t)(py * a.Pw + px);
+        const uint32_t win_bad = (uint32_t)!(py < a.Ph && px < a.Pw) << 31;
+        const bool q0 = lane & 1, q1 = (lane >> 1) & 1;
+        const int e = 2 * q0 + q1;
+        // SG: per-channel direction factors; without (all_max) the chains
+        // take the raw values.  (one uniform branch around two compile-time
+        // forms)
+        auto extrema = [&](auto sgc) X3_INLINE {
+          constexpr bool SG = decltype(sgc)::value;
+  #pragma unroll
+          for (int mt = 0; mt < G::MT; ++mt)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int cq = co0 + mt * 32 + 8 * q + 4 * h;  // first channel
+              f32x4 sg = {1.0f, 1.0f, 1.0f, 1.0f};
+              if constexpr (SG) sg = *reinterpret_cast<const f32x4*>(&s_par[cq]);
+              f32x4 t;
+  #pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) {
+                float m = SG ? sg[e2] * acc[mt][0][4 * q + e2] : acc[mt][0][4 * q + e2];
+  #pragma unroll
+                for (int j = 1; j < G::NW; ++j)
+                  m = vmax(m, SG ? sg[e2] * acc[mt][j][4 * q + e2] : acc[mt][j][4 * q + e2]);
+                t[e2] = m;
+              }
+              f32x2 u = q0 ? t.hi : t.lo;
+              {
+                const f32x2 give = q0 ? t.lo : t.hi;
+  #pragma unroll
+                for (int k = 0; k < 2; ++k) u[k] = vmax(u[k], dpp<DPP_QUAD_XOR1>(give[k]));
+              }
+              const float r = vmax(q1 ? u.y : u.x, dpp<DPP_QUAD_XOR2>(q1 ? u.x : u.y));
+              float v = r;
+              if constexpr (SG) {
+                const f32x2 s2 = q0 ? sg.hi : sg.lo;
+                v = (q1 ? s2.y : s2.x) * r;
+              }
+              const int co = cq + e;
+              // NCHW: channel planes (padded channels fall past the end);
+              // NHWC: channels innermost (padded channels get the drop bit)
+              const uint32_t off =
+                  G::NHWC ? ((win_off * (uint32_t)a.Cout + (uint32_t)co) << 2) |
+                                win_bad | ((uint32_t)(co >= a.Cout) << 31)
+                          : (((uint32_t)co * PP + win_off) << 2) | win_bad;
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v),
+                                                    o_rsrc, off, 0, 0);
             }
-            f32x2 u = q0 ? t.hi : t.lo;
-            {
-              const f32x2 give = q0 ? t.lo : t.hi;
+        };
+        if (all_max)
+          extrema(std::false_type{});
+        else
+          extrema(std::true_type{});
+      } else {
+        // (2') Windows of any size k.  A tile's origin is a multiple of k
+        // on both axes and it covers thk x twk outputs, both multiples of
+        // k, so no window leaves its tile; a window whose row pk*py is past
+        // Ph (or column past Pw) is an incomplete floor-mode window and is
+        // dropped, and every conv output inside a kept window is inside
+        // the image.  As for 4x4 windows, only the extremum that the
+        // monotone GroupNorm-affine-scale map sends to the maximum is kept,
+        // as a maximum of sg*y.
+        const int pk = a.pk;
+        const __amdgpu_buffer_rsrc_t o_rsrc = out_rsrc(n);
+        // NCHW: channel planes; NHWC: channels innermost (padded channels
+        // get the drop bit)
+        auto win_store = [&](int co, int py, int px, bool ok, float v) X3_INLINE {
+          const uint32_t bad = (uint32_t)!ok << 31;
+          const uint32_t off =
+              G::NHWC ? (((uint32_t)(py * a.Pw + px) * (uint32_t)a.Cout + (uint32_t)co) << 2) |
+                            bad | ((uint32_t)(co >= a.Cout) << 31)
+                      : (((uint32_t)co * PP + (uint32_t)(py * a.Pw + px)) << 2) | bad;
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), o_rsrc,
+                                                off, 0, 0);
+        };
+        if (EPI != EPI_GN_POOLKL && pk == 1) {
+          // every conv output is its own window
 #pragma unroll
-              for (int k = 0; k < 2; ++k) u[k] = vmax(u[k], dpp<DPP_QUAD_XOR1>(give[k]));
+          for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int co = co0 + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+#pragma unroll
+              for (int j = 0; j < G::NW; ++j)
+                win_store(co, r_base + j, c, col_ok && j < nrow_ok, acc[mt][j][i]);
             }
-            const float r = vmax(q1 ? u.y : u.x, dpp<DPP_QUAD_XOR2>(q1 ? u.x : u.y));
-            float v = r;
-            if constexpr (SG) {
-              const f32x2 s2 = q0 ? sg.hi : sg.lo;
-              v = (q1 ? s2.y : s2.x) * r;
-            }
-            const int co = cq + e;
-            // NCHW: channel planes (padded channels fall past the end);
-            // NHWC: channels innermost (padded channels get the drop bit)
-            const uint32_t off =
-                G::NHWC ? ((win_off * (uint32_t)a.Cout + (uint32_t)co) << 2) |
-                              win_bad | ((uint32_t)(co >= a.Cout) << 31)
-                        : (((uint32_t)co * PP + win_off) << 2) | win_bad;
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v),
-                                                  o_rsrc, off, 0, 0);
+        } else if constexpr (EPI != EPI_GN_POOLKL) {
+          // k = 2: a window is 2 rows in-lane (the wave's rows start at a multiple
+          // of 4) x 2 adjacent lanes (columns start at a multiple of 32):
+          // the pair's halving exchange leaves window row 2*(r_base/2) + b0
+          // in lane half b0 = lane bit 0
+          const bool b0 = lane & 1;
+          const int py = (r_base >> 1) + b0, px = c >> 1;
+          const bool wok = py < a.Ph && px < a.Pw;
+          auto pairs = [&](auto sgc) X3_INLINE {
+            constexpr bool SG = decltype(sgc)::value;
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int co = co0 + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                const float sg = SG ? s_par[co] : 1.0f;
+                const float t0 = vmax(sg * acc[mt][0][i], sg * acc[mt][1][i]);
+                const float t1 = vmax(sg * acc[mt][2][i], sg * acc[mt][3][i]);
+                const float r = vmax(b0 ? t1 : t0, dpp<DPP_QUAD_XOR1>(b0 ? t0 : t1));
+                win_store(co, py, px, wok, SG ? sg * r : r);
+              }
+          };
+          if (all_max)
+            pairs(std::false_type{});
+          else
+            pairs(std::true_type{});
+        } else {
+          // k >= 3: windows cross wavefronts.  Each wave folds its rows of
+          // a window in-lane (its 4 rows meet at most 2 window rows when k
+          // >= 3) and merges the result into the tile's window buffer with
+          // an LDS float maximum; lanes of one window column meet at the
+          // same address.  After a workgroup barrier all threads store the
+          // buffer and reset it to -inf.  (The next write to the buffer
+          // comes after the next item's barrier.)
+          const int nwx = a.twk / pk, nwy = a.thk / pk, nwin = nwx * nwy;
+          const int wy0 = wm.row0 / pk;
+          const int split = (wy0 + 1) * pk - wm.row0;  // rows j < split: wy0
+          const int jlim = a.thk - wm.row0;             // rows j < jlim: in the tile
+          const int cl = wm.strip * 32 + l32;           // column in the tile
+          const bool lok = cl < a.twk;
+          const int wx = lok ? cl / pk : 0;
+          const int offA = min(wy0, nwy - 1) * nwx + wx;
+          const int offB = min(wy0 + 1, nwy - 1) * nwx + wx;
+          constexpr float NEG = -__builtin_inff();
+          auto fold = [&](auto sgc) X3_INLINE {
+            constexpr bool SG = decltype(sgc)::value;
+#pragma unroll
+            for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int chl = mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                const float sg = SG ? s_par[co0 + chl] : 1.0f;
+                float mA = NEG, mB = NEG;
+#pragma unroll
+                for (int j = 0; j < G::NW; ++j) {
+                  const float v = SG ? sg * acc[mt][j][i] : acc[mt][j][i];
+                  mA = (j < jlim && j < split) ? vmax(mA, v) : mA;
+                  mB = (j < jlim && j >= split) ? vmax(mB, v) : mB;
+                }
+                // (constant channel stride: the offset is an immediate)
+                float* w = s_win + chl * WINCH;
+                __hip_atomic_fetch_max(w + offA, lok ? mA : NEG, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_max(w + offB, lok ? mB : NEG, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+              }
+          };
+          if (all_max)
+            fold(std::false_type{});
+          else
+            fold(std::true_type{});
+          __syncthreads();
+          const int py0 = rt * a.thk / pk, px0 = ct * a.twk / pk;
+          // (exact: the fractional parts sit at least 0.5 / nwin away from
+          // an integer, far above the rounding of these small products)
+          const float rnw = 1.0f / (float)nwin, rnx = 1.0f / (float)nwx;
+          for (int idx = tid; idx < G::COUT * nwin; idx += G::NTHR) {
+            const int chl = (int)(((float)idx + 0.5f) * rnw);
+            const int wv = idx - chl * nwin;
+            const int wy = (int)(((float)wv + 0.5f) * rnx);
+            const int wxi = wv - wy * nwx;
+            float v = s_win[chl * WINCH + wv];
+            s_win[chl * WINCH + wv] = NEG;
+            const int co = co0 + chl, py = py0 + wy, px = px0 + wxi;
+            if (!all_max) v *= s_par[co];
+            win_store(co, py, px, py < a.Ph && px < a.Pw, v);
           }
-      };
-      if (all_max)
-        extrema(std::false_type{});
-      else
-        extrema(std::true_type{});
+        }
+      }
     }
   };
 

@@ -47,10 +47,44 @@ inline bool nhwc_aligned16(const x3::ConvArgs& a) {
          (((uintptr_t)a.w & 15u) == 0);
 }
 
+// GroupNorm with pooling windows of any size k (other than 4, which has its
+// own epilogue): tiles of 16 x 64 outputs trimmed to whole windows, rows to
+// a multiple of k, columns to a multiple of k (NHWC) or of lcm(k, 4) (NCHW:
+// tile columns then start on 16-byte boundaries for the 16-byte staging,
+// and the partial-slot count does not depend on the alignment of x).
+constexpr int kGnkTH = 16, kGnkTWC = 64, kGnkWaves = 8, kGnkMaxWindow = 16;
+inline int gnk_rows(int k) { return kGnkTH - kGnkTH % k; }
+inline int gnk_cols(int k, bool nhwc) {
+  const int g = (k % 4 == 0) ? 4 : (k % 2 == 0 ? 2 : 1);
+  const int m = nhwc ? k : k * 4 / g;
+  return m > kGnkTWC ? 0 : kGnkTWC - kGnkTWC % m;
+}
+// Windows the fused GroupNorm kernels pool: 4 (own epilogue) and 1..16.
+inline bool gn_fused_window(int k, bool nhwc) {
+  return k == 4 || (k >= 1 && k <= kGnkMaxWindow && gnk_cols(k, nhwc) > 0);
+}
+// partial slots per (sample, group or channel) of the window-k kernels
+inline int gn_pps_k(int Ho, int Wo, int k, bool nhwc) {
+  if (!gn_fused_window(k, nhwc) || k == 4) return 0;
+  const int th = gnk_rows(k), tw = gnk_cols(k, nhwc);
+  return ((Ho + th - 1) / th) * ((Wo + tw - 1) / tw) * kGnkWaves;
+}
+
 template <class G, int EPI>
 x3_status run_conv(x3::ConvArgs a, hipStream_t st) {
-  a.n_rt = (a.Ho + G::TH - 1) / G::TH;
-  a.n_ct = (a.Wo + G::TWC - 1) / G::TWC;
+  if constexpr (x3::gn_generic_k<EPI>()) {
+    static_assert(G::TH == kGnkTH && G::TWC == kGnkTWC && G::NWAVE == kGnkWaves,
+                  "window-k tiles");
+    if (!(a.pk >= 1 && a.pk <= kGnkMaxWindow) || gnk_cols(a.pk, G::NHWC) <= 0)
+      return fail(X3_EUNSUPPORTED, "pool window %d not compiled in", a.pk);
+    a.thk = gnk_rows(a.pk);
+    a.twk = gnk_cols(a.pk, G::NHWC);
+  } else {
+    a.thk = G::TH;
+    a.twk = G::TWC;
+  }
+  a.n_rt = (a.Ho + a.thk - 1) / a.thk;
+  a.n_ct = (a.Wo + a.twk - 1) / a.twk;
   const int64_t ntiles = (int64_t)a.B * a.n_rt * a.n_ct;
   const int64_t nchunk = (a.Cin + G::CC - 1) / G::CC;
   const int64_t ncb = (a.Cout + G::COUT - 1) / G::COUT;
@@ -155,6 +189,9 @@ x3_status launch_epi_gn(const x3::GnPlaneArgs& g, int64_t B, int groups,
 // GroupNorm path: the conv pass (partials + pooled extrema), then the
 // finalize pass over B*groups workgroups.
 x3_status launch_gn_pool(const x3::ConvArgs& a, hipStream_t st);
+// The same for pooling windows other than 4 (a.pk, 1..16), NCHW or NHWC x.
+x3_status launch_gn_poolk(const x3::ConvArgs& a, hipStream_t st);
+x3_status launch_gn_poolk_nhwc(const x3::ConvArgs& a, hipStream_t st);
 x3_status launch_gn_finalize(const x3::GnFinArgs& f, int nblocks,
                              hipStream_t st);
 // NHWC x: the fused conv with epilogue `epi` (EPI_MIN_TANH2,
@@ -171,6 +208,11 @@ int gn_pps(int Ho, int Wo, int Cin, int Cout);
 // group); any other group size takes per-channel partials.
 inline bool gn_partials_per_channel(int Cout, int groups) {
   return Cout / groups != 4;
+}
+// The window-k kernels for k >= 3 (LDS window buffer) always take
+// per-channel partials.
+inline bool gn_partials_per_channel(int Cout, int groups, int pool_k) {
+  return gn_partials_per_channel(Cout, groups) || (pool_k != 4 && pool_k >= 3);
 }
 // float4 partials per (sample, group) that the finalize merges.
 inline int gn_parts_per_group(int Ho, int Wo, int Cin, int Cout, int groups) {

@@ -243,23 +243,27 @@ X3_API x3_status x3_conv3x3_scale_min_nhwc_f32(const float* x, const float* w,
 
 namespace {
 // Workspace of the GroupNorm entry point: the statistics partials of the
-// fused kernel (pool 4), or the whole conv output followed (at a 256-byte
-// boundary) by one partial per (sample, channel) plane (other windows).
+// fused kernels (windows 1..16), or the whole conv output followed (at a
+// 256-byte boundary) by one partial per (sample, channel) plane (larger
+// windows, NCHW only).
 size_t split_y_bytes(const Shape& s) {
   return ((size_t)s.B * s.Cout * s.Ho * s.Wo * sizeof(float) + 255) / 256 * 256;
 }
 // Partials the finalize merges per (sample, group): one per wavefront tile,
 // times the group's channels where the partials are per channel.
-int gn_parts(const Shape& s, int groups, bool nhwc) {
-  if (!nhwc) return x3i::gn_parts_per_group(s.Ho, s.Wo, s.Cin, s.Cout, groups);
-  const int slots = x3i::gn_pps_nhwc(s.Ho, s.Wo, s.Cin, s.Cout);
-  return x3i::gn_partials_per_channel(s.Cout, groups) ? slots * (s.Cout / groups)
-                                                      : slots;
+int gn_slots(int Ho, int Wo, int Cin, int Cout, int pool_k, bool nhwc) {
+  if (pool_k != 4) return x3i::gn_pps_k(Ho, Wo, pool_k, nhwc);
+  return nhwc ? x3i::gn_pps_nhwc(Ho, Wo, Cin, Cout) : x3i::gn_pps(Ho, Wo, Cin, Cout);
+}
+int gn_parts(const Shape& s, int groups, int pool_k, bool nhwc) {
+  const int slots = gn_slots(s.Ho, s.Wo, s.Cin, s.Cout, pool_k, nhwc);
+  return x3i::gn_partials_per_channel(s.Cout, groups, pool_k) ? slots * (s.Cout / groups)
+                                                              : slots;
 }
 size_t gn_workspace(const Shape& s, int groups, int pool_k, bool nhwc) {
-  if (pool_k != 4)
+  if (!x3i::gn_fused_window(pool_k, nhwc))
     return split_y_bytes(s) + (size_t)s.B * s.Cout * sizeof(float4);
-  return (size_t)s.B * groups * gn_parts(s, groups, nhwc) * sizeof(float4);
+  return (size_t)s.B * groups * gn_parts(s, groups, pool_k, nhwc) * sizeof(float4);
 }
 
 x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
@@ -277,8 +281,9 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
                 H - 2, W - 2);
   if (Cout > x3::kMaxCout)
     return fail(X3_EUNSUPPORTED, "Cout=%d exceeds %d", Cout, x3::kMaxCout);
-  if (nhwc && pool_k != 4)
-    return fail(X3_EUNSUPPORTED, "NHWC: pool_k=%d not compiled in (4)", pool_k);
+  const bool fused = x3i::gn_fused_window(pool_k, nhwc);
+  if (nhwc && !fused)
+    return fail(X3_EUNSUPPORTED, "NHWC: pool_k=%d not compiled in (1..16)", pool_k);
   if ((uint64_t)Cin * H * W * 4 >= (1ull << 31))
     return fail(X3_EUNSUPPORTED, "one sample of x must be smaller than 2 GiB");
   // (the kernel works in 64-channel blocks: padded channels and groups
@@ -288,17 +293,16 @@ x3_status check_gn(int B, int Cin, int H, int W, int Cout, int groups,
                      ((W - 2 - pool_k) / pool_k + 1);
   const uint64_t cpad = (uint64_t)(Cout + 63) / 64 * 64;
   const uint64_t prows =
-      x3i::gn_partials_per_channel(Cout, groups) ? cpad : cpad / 4;
-  const uint64_t slots = nhwc ? x3i::gn_pps_nhwc(H - 2, W - 2, Cin, Cout)
-                              : x3i::gn_pps(H - 2, W - 2, Cin, Cout);
-  if (pool_k == 4 &&
+      x3i::gn_partials_per_channel(Cout, groups, pool_k) ? cpad : cpad / 4;
+  const uint64_t slots = fused ? gn_slots(H - 2, W - 2, Cin, Cout, pool_k, nhwc) : 0;
+  if (fused &&
       (cpad * P * 4 >= (1ull << 31) || prows * slots * 16 >= (1ull << 31)))
     return fail(X3_EUNSUPPORTED,
                 "one sample of out or of the workspace must be < 2 GiB");
-  // other windows take the split path: the conv output is stored whole
+  // larger windows take the split path: the conv output is stored whole
   // (and one group of it is indexed with 32 bits)
-  if (pool_k != 4 && (uint64_t)x3i::padded_cout(Cout) * (H - 2) * (W - 2) * 4 >=
-                         (1ull << 31))
+  if (!fused && (uint64_t)x3i::padded_cout(Cout) * (H - 2) * (W - 2) * 4 >=
+                    (1ull << 31))
     return fail(X3_EUNSUPPORTED, "one sample of the conv output must be < 2 GiB");
   s = Shape{B, Cin, H, W, Cout, H - 2, W - 2};
   return X3_OK;
@@ -416,9 +420,9 @@ x3_status gn_entry(const float* x, const float* w, const float* b,
   }
 
   hipStream_t st = (hipStream_t)stream;
-  if (pool_k != 4) {
-    // split path: conv output into the workspace, then the standalone
-    // GroupNorm -> scale -> pool -> clamp kernels
+  if (!x3i::gn_fused_window(pool_k, nhwc)) {
+    // split path (windows above 16): conv output into the workspace, then
+    // the standalone GroupNorm -> scale -> pool -> clamp kernels
     rc = x3i::launch_conv_store(base_args(x, w, b, (float*)workspace, s), st);
     if (rc != X3_OK) return rc;
     x3::GnPlaneArgs g{};
@@ -443,12 +447,16 @@ x3_status gn_entry(const float* x, const float* w, const float* b,
   a.Ph = Ph;
   a.Pw = Pw;
   a.groups = groups;
-  rc = nhwc ? x3i::launch_nhwc(a,
-                               x3i::gn_partials_per_channel(Cout, groups)
-                                   ? x3::EPI_GN_POOL_CH
-                                   : x3::EPI_GN_POOL,
-                               st)
-            : x3i::launch_gn_pool(a, st);
+  a.pk = pool_k;
+  if (pool_k != 4)
+    rc = nhwc ? x3i::launch_gn_poolk_nhwc(a, st) : x3i::launch_gn_poolk(a, st);
+  else
+    rc = nhwc ? x3i::launch_nhwc(a,
+                                 x3i::gn_partials_per_channel(Cout, groups)
+                                     ? x3::EPI_GN_POOL_CH
+                                     : x3::EPI_GN_POOL,
+                                 st)
+              : x3i::launch_gn_pool(a, st);
   if (rc != X3_OK) return rc;
 
   x3::GnFinArgs f{};
@@ -460,7 +468,7 @@ x3_status gn_entry(const float* x, const float* w, const float* b,
   f.groups = groups;
   f.cpg = Cout / groups;
   f.C = Cout;
-  f.pps = gn_parts(s, groups, nhwc);
+  f.pps = gn_parts(s, groups, pool_k, nhwc);
   f.plane = Ph * Pw;
   f.eps = eps;
   f.lo = lo;
