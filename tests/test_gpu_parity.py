@@ -77,6 +77,22 @@ def assert_close(got, ref, tol=TOL, what=""):
 # Shapes that exercise every tile configuration (output width picks the
 # column-tile width), ragged rows and columns, several tiles per sample,
 # and Cin not a multiple of the 8-channel K chunk.
+# Problems of at most 32768 output pixels run on one-row tiles with one
+# wavefront each (so a small problem still spreads over many CUs); the
+# "regular" variants below repeat the batch past that size so the same
+# ragged shapes also reach the tiles of the large workloads.
+SMALL_PIXELS = 32768
+
+
+def batched(shape, tiles):
+    """The shape as given ("small"), or with its batch raised past the
+    small-problem size ("regular")."""
+    B, Cin, H, W = shape
+    if tiles == "regular":
+        B = max(B, -(-(SMALL_PIXELS + 1) // ((H - 2) * (W - 2))))
+    return B, Cin, H, W
+
+
 SHAPES64 = [  # (B, Cin, H, W)
     (2, 16, 32, 32),     # Wo=30: 1 strip, single ragged tile
     (1, 3, 35, 35),      # Wo=33: 2 strips, 1 valid column in the 2nd
@@ -89,10 +105,11 @@ SHAPES64 = [  # (B, Cin, H, W)
 ]
 
 
+@pytest.mark.parametrize("tiles", ["small", "regular"])
 @pytest.mark.parametrize("shape", SHAPES64)
 @pytest.mark.parametrize("Cout", [64, 128])
-def test_scale_min_integer_bit_exact(shape, Cout):
-    B, Cin, H, W = shape
+def test_scale_min_integer_bit_exact(shape, Cout, tiles):
+    B, Cin, H, W = shape = batched(shape, tiles)
     say(f"scale_min int-exact {shape} Cout={Cout}")
     d = random_case("scale_min", B, Cin, H, W, Cout, seed=100 + Cin, dist="int")
     got = run_op("scale_min", d, scale=2.0)
@@ -110,19 +127,21 @@ def test_scale_min_negative_scale_integer_bit_exact(shape):
     assert np.array_equal(got.astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("tiles", ["small", "regular"])
 @pytest.mark.parametrize("shape", SHAPES64)
 @pytest.mark.parametrize("Cout", [64, 128])
-def test_min_tanh2_random(shape, Cout):
-    B, Cin, H, W = shape
+def test_min_tanh2_random(shape, Cout, tiles):
+    B, Cin, H, W = shape = batched(shape, tiles)
     say(f"min_tanh2 {shape} Cout={Cout}")
     d = random_case("min_tanh2", B, Cin, H, W, Cout, seed=200 + W)
     assert_close(run_op("min_tanh2", d), run_oracle("min_tanh2", d), what=f"{shape}/{Cout}")
 
 
+@pytest.mark.parametrize("tiles", ["small", "regular"])
 @pytest.mark.parametrize("shape", SHAPES64)
 @pytest.mark.parametrize("Cout", [64, 128])
-def test_mul_lrelu_gelu_random(shape, Cout):
-    B, Cin, H, W = shape
+def test_mul_lrelu_gelu_random(shape, Cout, tiles):
+    B, Cin, H, W = shape = batched(shape, tiles)
     say(f"mul_lrelu_gelu {shape} Cout={Cout}")
     d = random_case("mul_lrelu_gelu", B, Cin, H, W, Cout, seed=300 + H)
     assert_close(run_op("mul_lrelu_gelu", d), run_oracle("mul_lrelu_gelu", d),
@@ -248,10 +267,11 @@ SHAPES_C = [  # (B, Cin, H, W)
 ]
 
 
+@pytest.mark.parametrize("tiles", ["small", "regular"])
 @pytest.mark.parametrize("shape", SHAPES_C)
 @pytest.mark.parametrize("Cout", COUTS)
-def test_any_cout_scale_min_integer_bit_exact(shape, Cout):
-    B, Cin, H, W = shape
+def test_any_cout_scale_min_integer_bit_exact(shape, Cout, tiles):
+    B, Cin, H, W = shape = batched(shape, tiles)
     say(f"scale_min int-exact {shape} Cout={Cout}")
     d = random_case("scale_min", B, Cin, H, W, Cout, seed=800 + Cout, dist="int")
     for scale in (2.0, -1.0):

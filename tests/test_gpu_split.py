@@ -151,7 +151,8 @@ def test_epi_gn_pooled_block_beyond_lds(groups):
     assert_close(got, ref, what=f"groups={groups}")
 
 
-SHAPES = [(2, 16, 32, 32), (1, 12, 20, 67), (1, 16, 11, 131), (1, 20, 7, 300)]
+SHAPES = [(2, 16, 32, 32), (1, 12, 20, 67), (1, 16, 11, 131), (1, 20, 7, 300),
+          (20, 8, 34, 70), (10, 5, 30, 132)]  # (the last two: past the one-row-tile size)
 
 
 @pytest.mark.parametrize("shape", SHAPES)

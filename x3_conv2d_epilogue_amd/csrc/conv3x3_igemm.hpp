@@ -662,7 +662,7 @@ __global__ void __launch_bounds__(G::NTHR)
   // per-group partials (groups of 4 channels) or per-channel partials
   constexpr bool GN_CH =
       EPI == EPI_GN_POOL_CH || EPI == EPI_GN_POOLK_CH || EPI == EPI_GN_POOLKL;
-  constexpr int NPEND = DEFER ? G::NW / 2 : 1;
+  constexpr int NPEND = (DEFER && G::NW > 1) ? G::NW / 2 : 1;
   constexpr uint32_t DROP = 0x80000000u;
   uint32_t pend_v[NPEND], pend_off[NPEND];
 #pragma unroll
@@ -723,7 +723,7 @@ __global__ void __launch_bounds__(G::NTHR)
       // then across the two lane halves (which hold the other channels of
       // the same pixels).  Half 0 finishes pixel rows 0..NW/2-1 and half 1
       // rows NW/2..NW-1, so every lane evaluates and stores NW/2 results.
-      static_assert(G::NW % 2 == 0, "lane halves split the N-tiles");
+      static_assert(G::NW % 2 == 0 || G::NW == 1, "lane halves split the N-tiles");
       constexpr int HN = G::NW / 2;
       const bool use_max = (EPI == EPI_SCALE_MIN) && !(a.s0 >= 0.0f);
       float m[G::NW];
@@ -756,20 +756,30 @@ __global__ void __launch_bounds__(G::NTHR)
         }
         if (cb != a.ncb - 1) return;  // more channel blocks to come
       }
+      auto finish = [&](float v) X3_INLINE {
+        if constexpr (EPI == EPI_MIN_TANH2)
+          return tanhf(tanhf(v));
+        else
+          return a.s0 * v;
+      };
+      if constexpr (G::NW == 1) {
+        // one pixel row: both halves hold the full extremum after the
+        // exchange, half 0 stores it
+        const float recv = shfl_xor(m[0], 32);
+        const float v = use_max ? fmaxf(m[0], recv) : fminf(m[0], recv);
+        pend_v[0] = __builtin_bit_cast(uint32_t, finish(v));
+        pend_off[0] = ((uint32_t)(r_base * a.Wo + c) << 2) |
+                      ((uint32_t)!(col_ok && r_base < a.Ho && h == 0) << 31);
+      }
 #pragma unroll
       for (int jj = 0; jj < HN; ++jj) {
         const float keep = h ? m[jj + HN] : m[jj];
         const float recv = shfl_xor(h ? m[jj] : m[jj + HN], 32);
         const float v = use_max ? fmaxf(keep, recv) : fminf(keep, recv);
         const int r = r_base + jj + h * HN;
-        float y;
-        if constexpr (EPI == EPI_MIN_TANH2)
-          y = tanhf(tanhf(v));
-        else
-          y = a.s0 * v;
         // bounded store into this sample's output plane (parked for the
         // next item's loop); bit 31 drops it
-        pend_v[jj] = __builtin_bit_cast(uint32_t, y);
+        pend_v[jj] = __builtin_bit_cast(uint32_t, finish(v));
         pend_off[jj] = ((uint32_t)(r * a.Wo + c) << 2) |
                        ((uint32_t)!(col_ok && r < a.Ho) << 31);
       }

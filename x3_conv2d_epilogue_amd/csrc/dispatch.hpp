@@ -98,8 +98,9 @@ x3_status run_conv(x3::ConvArgs a, hipStream_t st) {
   // resident weights: one channel block, at most RC K chunks
   if (G::RESW && (ncb != 1 || nchunk > G::RC))
     return fail(X3_EUNSUPPORTED, "resident-weight configuration misapplied");
-  // one workgroup per CU resident (two for the 4-wave configurations)
-  const int cus = num_cus() * (G::NWAVE == 4 ? 2 : 1);
+  // one workgroup per CU resident (two for the 4-wave configurations and
+  // the one-wave small tiles)
+  const int cus = num_cus() * (G::NWAVE < 8 ? 2 : 1);
   const int64_t grid = ntiles < cus ? ntiles : cus;
   if (ntiles >= (1ll << 31) || (ntiles / grid + 1) * ncb * nchunk >= (1ll << 31))
     return fail(X3_EUNSUPPORTED, "problem too large for 32-bit item counters");
@@ -165,8 +166,28 @@ x3_status dispatch_x4(const x3::ConvArgs& a, hipStream_t st) {
   return mt == 4 ? dispatch_mt4<EPI, true, NH>(a, st) : dispatch_mt2<EPI, true, NH>(a, st);
 }
 
+// Problems too small to fill the GPU with the tiles above (at most
+// kSmallPixels output pixels, e.g. [2,16,32,32] -> 30x30: two 32x32 tiles
+// for 256 CUs): tiles of one row of 32 columns with one wavefront each,
+// so the work spreads over many CUs and each wavefront's chain of matrix
+// instructions is short.
+constexpr int64_t kSmallPixels = 32768;
+template <int EPI, bool X4>
+x3_status dispatch_small(const x3::ConvArgs& a, hipStream_t st) {
+  const int mt = channel_block_mt(a.Cout);
+  const bool res = X4 && a.Cin <= 16 && a.Cout <= 32 * mt;
+  if (mt == 4)
+    return res ? run_conv<x3::Geo<4, 8, 1, 1, 1, true, 2>, EPI>(a, st)
+               : run_conv<x3::Geo<4, 8, 1, 1, 1, X4, 0>, EPI>(a, st);
+  return res ? run_conv<x3::Geo<2, 8, 1, 1, 1, true, 2>, EPI>(a, st)
+             : run_conv<x3::Geo<2, 8, 1, 1, 1, X4, 0>, EPI>(a, st);
+}
+
 template <int EPI>
 x3_status dispatch(const x3::ConvArgs& a, hipStream_t st) {
+  if ((int64_t)a.B * a.Ho * a.Wo <= kSmallPixels)
+    return rows_aligned16(a) ? dispatch_small<EPI, true>(a, st)
+                             : dispatch_small<EPI, false>(a, st);
   if (rows_aligned16(a)) return dispatch_x4<EPI, false>(a, st);
   if (channel_block_mt(a.Cout) == 4) return dispatch_mt4<EPI, false>(a, st);
   return dispatch_mt2<EPI, false>(a, st);
