@@ -206,8 +206,6 @@ struct Geo {
   static constexpr int NBW = (NBWT + NWAVE - 1) / NWAVE;  // per wave
   static constexpr int STAGE = XBUF + (RESW ? 0 : WBUF);
   static constexpr int LDS_DWORDS = 2 * STAGE + RC * WBUF;
-  // blocks each wave stages per item
-  static constexpr int NB_ITEM = NBI + (RESW ? 0 : NBW);
   static constexpr int KS = KC / 2;       // MFMA k-steps per chunk
   static constexpr int NTILE_N = TH * NCT;  // N-tiles per workgroup tile
   static constexpr int NW = NTILE_N / NWAVE;  // N-tiles per wave
@@ -459,7 +457,24 @@ __global__ void __launch_bounds__(G::NTHR)
   // blocks; bit 31 set = never loaded (stage padding past CC channels,
   // weight-row padding past K).
   uint32_t xoff[PRE ? G::NBI : 1];
-  uint32_t woff[PRE ? G::NBW : 1], wkk[PRE ? G::NBW : 1];
+  // NH4 weight rows in the order the K walk reads them (PW): a weight row
+  // holds K index (4h + e)*9 + tap at dword 36h + 4*tap + e, so a lane's
+  // weights for the 4 k-steps of a tap are 4 consecutive dwords (one
+  // conflict-free ds_read_b128, as in KO).  The permutation moves single
+  // floats, so those rows are staged with 4-byte loads, NBWP blocks of 64
+  // dwords per wave, each with its per-lane source offset kept in a
+  // register while the weights are staged per item.  Taken with resident
+  // weights (staged once) and with 64-channel blocks; 128-channel blocks
+  // staged per item read the unpermuted rows with 4-byte fragment reads
+  // (their 19 four-byte weight loads per wave and item cost more than the
+  // bank conflicts they remove), and so do the pooling-window epilogues
+  // with staged weights (no registers left for the offsets).
+  constexpr bool PW =
+      G::NH4 && (G::RESW || (G::MT == 2 && !gn_generic_k<EPI>()));
+  constexpr int NBWTP = G::WBUF / 64;                     // 4-byte weight blocks
+  constexpr int NBWP = (NBWTP + G::NWAVE - 1) / G::NWAVE;  // per wave
+  constexpr int NBWK = PW ? NBWP : G::NBW;  // weight blocks per wave
+  uint32_t woff[PRE ? NBWK : 1], wkk[PRE && !PW ? G::NBW : 1];
   constexpr int RBLK = G::RSZ / 256;  // NH4: blocks per channel-half region
   if constexpr (G::NH4) {
 #pragma unroll
@@ -492,7 +507,24 @@ __global__ void __launch_bounds__(G::NTHR)
                 ((uint32_t)(cil >= (uint32_t)G::CC) << 31);
     }
   }
-  if constexpr (PRE) {
+  if constexpr (PW) {
+#pragma unroll
+    for (int i = 0; i < NBWP; ++i) {
+      int blk = wave + i * G::NWAVE;
+      blk = blk < NBWTP - 1 ? blk : NBWTP - 1;
+      // LDS dword j of row co <- K index (4h + e)*9 + tap; dwords past the
+      // 72 of a row are padding (read as zero); bit 30 marks the upper
+      // channel half, which a last chunk of 4 channels masks
+      const uint32_t q = (uint32_t)(blk * 64 + lane);
+      const uint32_t co = q / G::WP;
+      const uint32_t j = q - co * G::WP;
+      const uint32_t hh = j >= (uint32_t)G::KS;
+      const uint32_t r = j - hh * (uint32_t)G::KS;
+      const uint32_t kk = (4u * hh + (r & 3u)) * 9u + (r >> 2);
+      woff[i] = ((co * (uint32_t)CinK + kk) << 2) | (hh << 30) |
+                ((uint32_t)(j >= (uint32_t)G::KC) << 31);
+    }
+  } else if constexpr (PRE) {
 #pragma unroll
     for (int i = 0; i < G::NBW; ++i) {
       int blk = wave + i * G::NWAVE;
@@ -563,6 +595,18 @@ __global__ void __launch_bounds__(G::NTHR)
             (uint32_t)l.base) << 2) | ((uint32_t)!ok << 31);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           l.xr, (X3_LDS void*)(sbase + blk * G::XBLK), 4, off, 0, 0, 0);
+    } else if constexpr (PW) {
+      const int iw = i - G::NBI;
+      int blk = wave + iw * G::NWAVE;
+      blk = blk < NBWTP - 1 ? blk : NBWTP - 1;
+      X3_LDS float* wdst =
+          G::RESW ? (X3_LDS float*)ldsw + l.wslot * G::WBUF : sbase + G::XBUF;
+      // (Cin % 4 == 0: a short last chunk has 4 channels, K = 36)
+      const uint32_t hi = (woff[iw] >> 30) & 1u;
+      const uint32_t off = (woff[iw] & ~(1u << 30)) |
+                           ((hi & (uint32_t)(l.kk_lim <= G::KS)) << 31);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          l.wr, (X3_LDS void*)(wdst + blk * 64), 4, off, 0, 0, 0);
     } else {
       const int iw = i - G::NBI;
       int blk = wave + (PRE ? 0 : zz) + iw * G::NWAVE;
@@ -591,7 +635,7 @@ __global__ void __launch_bounds__(G::NTHR)
 
   // blocks per wave per item, BPS per k-step over the first half of the
   // k-steps, so that they have the second half to land
-  constexpr int NB_W = G::NB_ITEM;
+  constexpr int NB_W = G::NBI + (G::RESW ? 0 : NBWK);
   constexpr int KS_ISSUE = G::KS / 2 > 0 ? G::KS / 2 : 1;
   constexpr int BPS = (NB_W + KS_ISSUE - 1) / KS_ISSUE;
 
@@ -1294,8 +1338,9 @@ __global__ void __launch_bounds__(G::NTHR)
         : G::KO   ? cur + h * (G::CC / 2) * G::CS + wm.row0 * G::XP +
                         wm.strip * 32 + l32
                   : cur + h * G::CS + wm.row0 * G::XP + wm.strip * 32 + l32;
-    // (a weight row holds K index ci*9 + tap; lane half h starts at channel
-    // CC/2 * h for KO and NH4, which is K index 36h = KS*h)
+    // (a weight row holds K index ci*9 + tap, or with PW channel 4h + e of
+    // tap t at dword 36h + 4t + e; lane half h starts at channel CC/2 * h
+    // for KO and NH4, which is dword 36h = KS*h either way)
     const X3_LDS float* ws =
         (G::RESW ? (const X3_LDS float*)ldsw + chunk * G::WBUF
                  : cur + G::XBUF) + l32 * G::WP + h * (G::X4 ? G::KS : 9);
@@ -1303,10 +1348,11 @@ __global__ void __launch_bounds__(G::NTHR)
     // fragment reads of step s+1, its share of the next item's staging
     // loads, then its MFMAs; a scheduling fence keeps that order, so each
     // MFMA's operands were requested a full step (MT*NW MFMAs) earlier.
-    // KO reads the weights of 4 k-steps at once, a group ahead; NH4 reads
-    // the input values of the 4 k-steps of a tap at once, a tap ahead.
+    // KO and PW read the weights of 4 k-steps at once, a group ahead; NH4
+    // reads the input values of the 4 k-steps of a tap at once, a tap ahead.
     float av[2][G::MT], bv[2][G::NW];
-    f32x4 a4[2][G::KO ? G::MT : 1];
+    constexpr bool A4 = G::KO || PW;  // weights of 4 k-steps in one read
+    f32x4 a4[2][A4 ? G::MT : 1];
     f32x4 b4[2][G::NH4 ? G::NW : 1];
     auto load_b4 = [&](int tap, f32x4 (&Bq)[G::NH4 ? G::NW : 1]) X3_INLINE {
       const int kh = tap / 3, kw = tap % 3;
@@ -1315,19 +1361,23 @@ __global__ void __launch_bounds__(G::NTHR)
         Bq[j] = *reinterpret_cast<const X3_LDS f32x4*>(
             xs + ((j + kh) * G::XCOLS + kw) * 4);
     };
-    auto load_a4 = [&](int g, f32x4 (&A)[G::KO ? G::MT : 1]) X3_INLINE {
+    auto load_a4 = [&](int g, f32x4 (&A)[A4 ? G::MT : 1]) X3_INLINE {
 #pragma unroll
-      for (int mt = 0; mt < (G::KO ? G::MT : 1); ++mt)
+      for (int mt = 0; mt < (A4 ? G::MT : 1); ++mt)
         A[mt] = *reinterpret_cast<const X3_LDS f32x4*>(ws + mt * 32 * G::WP +
                                                        4 * g);
     };
     auto load_frag = [&](int s, float (&A)[G::MT], float (&Bv)[G::NW]) X3_INLINE {
       if constexpr (G::NH4) {
-        // k-step s: tap s/4, channel 4h + s%4 (K index (4h + s%4)*9 + tap)
-        const int tap = s / 4, cq = s % 4;
+        // k-step s: tap s/4, channel 4h + s%4 (K index (4h + s%4)*9 + tap);
+        // with PW its weights come with the group's ds_read_b128
+        if constexpr (!PW) {
+          const int tap = s / 4, cq = s % 4;
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt)
-          A[mt] = ws[mt * 32 * G::WP + cq * 9 + tap];
+          for (int mt = 0; mt < G::MT; ++mt)
+            A[mt] = ws[mt * 32 * G::WP + cq * 9 + tap];
+        }
+        (void)A;
         (void)Bv;
       } else if constexpr (G::KO) {
         const int ci = s / 9, tap = s % 9, kh = tap / 3, kw = tap % 3;
@@ -1347,12 +1397,12 @@ __global__ void __launch_bounds__(G::NTHR)
                           : xs[2 * cp * G::CS + (j + kh) * G::XP + kw];
       }
     };
-    if constexpr (G::KO) load_a4(0, a4[0]);
+    if constexpr (A4) load_a4(0, a4[0]);
     if constexpr (G::NH4) load_b4(0, b4[0]);
     load_frag(0, av[0], bv[0]);
 #pragma unroll
     for (int s = 0; s < G::KS; ++s) {
-      if constexpr (G::KO) {
+      if constexpr (A4) {
         if (s % 4 == 0 && s / 4 + 1 < G::KS / 4)
           load_a4(s / 4 + 1, a4[(s / 4 + 1) & 1]);
       }
@@ -1376,7 +1426,7 @@ __global__ void __launch_bounds__(G::NTHR)
 #pragma unroll
         for (int j = 0; j < G::NW; ++j)
           acc[mt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-              G::KO ? a4[(s / 4) & 1][mt][s % 4] : av[s & 1][mt],
+              A4 ? a4[(s / 4) & 1][mt][s % 4] : av[s & 1][mt],
               G::NH4 ? b4[(s / 4) & 1][G::NH4 ? j : 0][s % 4] : bv[s & 1][j],
               acc[mt][j], 0, 0, 0);
       // Issue order inside the step: each MFMA (64 cycles in the matrix
@@ -1420,7 +1470,7 @@ __global__ void __launch_bounds__(G::NTHR)
           lc.kk_lim = kl < G::KC ? kl : G::KC;
           lc.wslot = c;
 #pragma unroll
-          for (int i = G::NBI; i < G::NBI + G::NBW; ++i)
+          for (int i = G::NBI; i < G::NBI + NBWK; ++i)
             issue(lc, (X3_LDS float*)lds0, i, 0);
         }
       }

@@ -46,6 +46,13 @@ inline bool nhwc_aligned16(const x3::ConvArgs& a) {
   return (a.Cin % 4 == 0) && (((uintptr_t)a.x & 15u) == 0) &&
          (((uintptr_t)a.w & 15u) == 0);
 }
+// The NHWC 16-byte configurations that stage permuted weight rows keep a
+// flag in bit 30 of each weight offset, so the offsets inside a 128-row
+// channel block must stay below 1 GiB (Cin < 233,017); larger Cin takes
+// the 4-byte configurations.
+inline bool nhwc_x4_weights_fit(const x3::ConvArgs& a) {
+  return (int64_t)128 * a.Cin * 9 * 4 < (int64_t(1) << 30);
+}
 
 // GroupNorm with pooling windows of any size k (other than 4, which has its
 // own epilogue): tiles of 16 x 64 outputs trimmed to whole windows, rows to

@@ -30,7 +30,7 @@ x3_status dispatch_nhwc_mt2(const x3::ConvArgs& a, hipStream_t st) {
 
 template <int EPI>
 x3_status dispatch_nhwc(const x3::ConvArgs& a, hipStream_t st) {
-  if (nhwc_aligned16(a)) return dispatch_x4<EPI, true>(a, st);
+  if (nhwc_aligned16(a) && nhwc_x4_weights_fit(a)) return dispatch_x4<EPI, true>(a, st);
   if (channel_block_mt(a.Cout) == 4) {
     if (a.Wo > 64) return run_conv<GeoN<4, 4, 4>, EPI>(a, st);
     if (a.Wo > 32) return run_conv<GeoN<4, 8, 2>, EPI>(a, st);
@@ -43,7 +43,7 @@ x3_status dispatch_nhwc(const x3::ConvArgs& a, hipStream_t st) {
 // ones, so the GroupNorm partial slots do not depend on the alignment)
 template <int EPI>
 x3_status dispatch_gn_nhwc(const x3::ConvArgs& a, hipStream_t st) {
-  if (nhwc_aligned16(a)) {
+  if (nhwc_aligned16(a) && nhwc_x4_weights_fit(a)) {
     if (gn_resident_nhwc(a.Cin, a.Cout)) {
       if (a.Wo > 32) return run_conv<x3::Geo<2, 8, 8, 2, 4, true, 1, true>, EPI>(a, st);
       return run_conv<x3::Geo<2, 8, 16, 1, 4, true, 1, true>, EPI>(a, st);
