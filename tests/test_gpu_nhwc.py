@@ -106,6 +106,24 @@ def test_nhwc_gn_pool(shape, cg):
                                           n["scale"], groups, 1e-5, 4, -50.0, 50.0), "gn")
 
 
+@pytest.mark.parametrize("case", [
+    ((1, 8, 200, 130), 64, 16),   # 200 partials per group: the finalize's looped merge
+    ((2, 8, 34, 34), 30, 10),     # 30 channels: the finalize's 4-byte accesses
+    ((1, 16, 12, 40), 128, 128),  # 128 groups of one channel
+])
+def test_nhwc_gn_pool_finalize_paths(case):
+    (B, Cin, H, W), Cout, groups = case
+    say(f"nhwc gn finalize {case}")
+    d = random_case("gn_scale_pool_clamp", B, Cin, H, W, Cout, seed=1900 + Cout + groups)
+    d["gamma"][1::4] *= -1.0
+    g = dev_cl(d)
+    out = x3.conv3x3_gn_scale_pool_clamp(g["x"], g["weight"], g["bias"], g["gamma"], g["beta"],
+                                         g["scale"], groups, 1e-5, 4, -50.0, 50.0)
+    n = {k: v.numpy() for k, v in d.items()}
+    close(out, oracle.gn_scale_pool_clamp(n["x"], n["weight"], n["bias"], n["gamma"], n["beta"],
+                                          n["scale"], groups, 1e-5, 4, -50.0, 50.0), "gn")
+
+
 def test_nhwc_matches_nchw_on_full_width_shape():
     """One larger shape through both layouts: identical inputs, results
     within fp32 rounding of each other (the two layouts sum the K terms in

@@ -1647,9 +1647,14 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
 // it with 16-byte accesses (VEC: C % 4 == 0, out 16-byte aligned), after
 // merging the statistics of every group of the sample (one wavefront per
 // group at a time; the partials are few and L2-resident) into per-channel
-// constants in LDS.  (Requesting the chunk before the merge was measured
-// slower: those loads then queue ahead of the partials the merge waits
-// for.)
+// constants in LDS.
+// When a wavefront has at most four groups of at most 128 partials and 64
+// channels (the usual case), it requests its partials (two per lane and
+// group) and its lanes' channel parameters first, then the thread's share
+// of the chunk, and merges while the chunk is in flight: the merge waits
+// only for what was issued ahead of the chunk.  (Requesting the chunk ahead of the partials was measured
+// slower: the merge then waits behind those loads.)  Otherwise the
+// partials are read in a loop after the chunk has been requested.
 // The merge is one pass over the partials in double: with s_k = sum_k,
 // N = sum n_k, mean = sum s_k / N and
 //   M2 = sum_k M2_k + sum_k n_k (s_k/n_k - mean)^2
@@ -1663,12 +1668,13 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
-constexpr int kFinNhwcThreads = 512;
+constexpr int kFinNhwcThreads = 1024;
 constexpr int kFinNhwcPerThread = 8;  // float4 (or floats) per thread
 
 template <int NT, bool VEC>
 __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a) {
   __shared__ float s_mu[kMaxCout], s_A[kMaxCout], s_B[kMaxCout];
+  constexpr int NWV = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = blockIdx.x / a.nchunk, chunk = blockIdx.x - n * a.nchunk;
   float* o = a.out + (size_t)n * a.plane * a.C;
@@ -1677,25 +1683,103 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
   const int nel = VEC ? total / 4 : total;
   const int beg = chunk * span;
   const int end = min(beg + span, nel);
-  for (int g = wave; g < a.groups; g += NT / 64) {
-    const float4* p = a.part + ((size_t)n * a.groups + g) * a.pps;
-    double sum = 0.0, sq = 0.0;
-    for (int k = lane; k < a.pps; k += 64) {
-      const float4 v = p[k];
-      if (v.z > 0.0f) {
-        sum += (double)v.x;
-        sq += (double)v.y + (double)v.x * (double)v.x / (double)v.z;
+  const float4* pn = a.part + (size_t)n * a.groups * a.pps;
+
+  // Loads through raw buffer resources: an element that must not be read
+  // gets bit 31 set in its offset (past num_records, read as zero), so the
+  // loads need no branches.
+  // (uniform) the wavefront's partials, and its lanes' channel parameters
+  // (lane l: channel l of the group), fit in registers
+  constexpr int GPW = 4;  // groups per wavefront held in registers
+  const bool held = a.groups <= GPW * NWV && a.pps <= 128 && a.cpg <= 64;
+  float4 pv[GPW][2];
+  float gam[GPW], bet[GPW], sca[GPW];
+  if (held) {
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(pn, (uint32_t)(a.groups * a.pps) * 16u);
+    const uint32_t cbytes = (uint32_t)(a.groups * a.cpg) * 4u;
+    const __amdgpu_buffer_rsrc_t gr = make_rsrc(a.gamma, cbytes);
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(a.beta, cbytes);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(a.scale, cbytes);
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = wave + gi * NWV;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int k = lane + 64 * r;
+        const uint32_t off = ((uint32_t)(g * a.pps + k) << 4) |
+                             ((uint32_t)!(g < a.groups && k < a.pps) << 31);
+        pv[gi][r] = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
       }
+      const uint32_t coff = ((uint32_t)(g * a.cpg + lane) << 2) |
+                            ((uint32_t)!(g < a.groups && lane < a.cpg) << 31);
+      gam[gi] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, coff, 0, 0));
+      bet[gi] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, coff, 0, 0));
+      sca[gi] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, coff, 0, 0));
     }
+  }
+  // this thread's share of the chunk
+  const __amdgpu_buffer_rsrc_t orr = make_rsrc(o, (uint32_t)total * 4u);
+  float4 v4[VEC ? kFinNhwcPerThread : 1];
+  float v1[VEC ? 1 : kFinNhwcPerThread];
+#pragma unroll
+  for (int r = 0; r < kFinNhwcPerThread; ++r) {
+    const int k = beg + tid + r * NT;
+    const uint32_t bad = (uint32_t)(k >= end) << 31;
+    if constexpr (VEC)
+      v4[r] = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(orr, ((uint32_t)k << 4) | bad, 0, 0));
+    else
+      v1[r] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(orr, ((uint32_t)k << 2) | bad, 0, 0));
+  }
+
+  // group g's mean and 1/sigma from the wavefront's sums
+  auto stats = [&](double sum, double sq, float& mu, float& rstd) {
     sum = wave_sum_d<NT>(sum);
     sq = wave_sum_d<NT>(sq);
     const double mean = sum / a.count;
     const double m2 = fmax(sq - sum * mean, 0.0);
-    const float rstd = (float)(1.0 / sqrt(m2 / a.count + (double)a.eps));
-    for (int c = g * a.cpg + lane; c < (g + 1) * a.cpg; c += 64) {
-      s_mu[c] = (float)mean;
-      s_A[c] = rstd * a.gamma[c] * a.scale[c];
-      s_B[c] = a.beta[c] * a.scale[c];
+    mu = (float)mean;
+    rstd = (float)(1.0 / sqrt(m2 / a.count + (double)a.eps));
+  };
+  auto add = [](const float4 v, double& sum, double& sq) {
+    if (v.z > 0.0f) {
+      sum += (double)v.x;
+      sq += (double)v.y + (double)v.x * (double)v.x / (double)v.z;
+    }
+  };
+  if (held) {
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = wave + gi * NWV;
+      if (g < a.groups) {
+        double sum = 0.0, sq = 0.0;
+        add(pv[gi][0], sum, sq);
+        add(pv[gi][1], sum, sq);
+        float mu, rstd;
+        stats(sum, sq, mu, rstd);
+        if (lane < a.cpg) {
+          const int c = g * a.cpg + lane;
+          s_mu[c] = mu;
+          s_A[c] = rstd * gam[gi] * sca[gi];
+          s_B[c] = bet[gi] * sca[gi];
+        }
+      }
+    }
+  } else {
+    for (int g = wave; g < a.groups; g += NWV) {
+      const float4* p = pn + (size_t)g * a.pps;
+      double sum = 0.0, sq = 0.0;
+      for (int k = lane; k < a.pps; k += 64) add(p[k], sum, sq);
+      float mu, rstd;
+      stats(sum, sq, mu, rstd);
+      for (int c = g * a.cpg + lane; c < (g + 1) * a.cpg; c += 64) {
+        s_mu[c] = mu;
+        s_A[c] = rstd * a.gamma[c] * a.scale[c];
+        s_B[c] = a.beta[c] * a.scale[c];
+      }
     }
   }
   __syncthreads();
@@ -1705,7 +1789,7 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
     if (k >= end) continue;
     if constexpr (VEC) {
       const int c = (4 * k) % a.C;  // 4 consecutive channels (C % 4 == 0)
-      float4 v = reinterpret_cast<const float4*>(o)[k];
+      float4 v = v4[r];
       v.x = fminf(fmaxf(fmaf(v.x - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
       v.y = fminf(fmaxf(fmaf(v.y - s_mu[c + 1], s_A[c + 1], s_B[c + 1]), a.lo), a.hi);
       v.z = fminf(fmaxf(fmaf(v.z - s_mu[c + 2], s_A[c + 2], s_B[c + 2]), a.lo), a.hi);
@@ -1713,7 +1797,7 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
       reinterpret_cast<float4*>(o)[k] = v;
     } else {
       const int c = k % a.C;
-      o[k] = fminf(fmaxf(fmaf(o[k] - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
+      o[k] = fminf(fmaxf(fmaf(v1[r] - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
     }
   }
 }
