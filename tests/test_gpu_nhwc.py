@@ -64,6 +64,20 @@ def test_nhwc_scale_min_integer_bit_exact(shape, Cout):
         assert np.array_equal(got.astype(np.float64), ref), f"scale {s}"
 
 
+@pytest.mark.parametrize("Cin", [233016, 233020])
+def test_nhwc_weight_offsets_near_the_16_byte_bound(Cin):
+    """The 16-byte NHWC kernels that stage permuted weight rows keep a flag
+    in bit 30 of each weight offset, so Cin >= 233,017 takes the 4-byte
+    kernels.  One output pixel on each side of that bound, integer inputs
+    (every fp32 partial sum exact), bit-exact against the oracle."""
+    say(f"nhwc scale_min int-exact Cin={Cin}")
+    d = random_case("scale_min", 1, Cin, 3, 3, 64, seed=1600, dist="int")
+    g = dev_cl(d)
+    got = x3.conv3x3_scale_min(g["x"], g["weight"], g["bias"], 2.0).cpu().numpy()
+    ref = oracle.scale_min(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(), 2.0)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("Cout", [64, 128])
 def test_nhwc_min_tanh2(shape, Cout):
