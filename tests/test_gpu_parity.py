@@ -391,6 +391,31 @@ def _sample_pixels(B, Ho, Wo, n, seed):
     return np.concatenate([np.array(fixed, np.int64), rand.astype(np.int64)])
 
 
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+def test_edge_sample_just_under_2gib(layout):
+    """One sample of x just under the 2 GiB per-sample limit (64 x 2896 x
+    2896 floats, 99.98 % of 2^31 bytes): 32-bit buffer offsets and their
+    out-of-range flag at their largest, 12 ragged column tiles.  Sampled
+    against the oracle, the image's edges and tile seams included."""
+    B, Cin, H, W, Cout = 1, 64, 2896, 2896, 128
+    assert Cin * H * W * 4 < 2**31
+    say(f"near-2GiB sample {layout}")
+    d = random_case("scale_min", B, Cin, H, W, Cout, seed=2100)
+    g = to_dev(d)
+    if layout == "nhwc":
+        g["x"] = g["x"].contiguous(memory_format=torch.channels_last)
+        assert x3.is_nhwc(g["x"])
+    got = x3.conv3x3_scale_min(g["x"], g["weight"], g["bias"], 2.0)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    del g
+    torch.cuda.empty_cache()
+    assert got.shape == (B, 1, H - 2, W - 2)
+    pix = _sample_pixels(B, H - 2, W - 2, 1500, 5)
+    ref = oracle.scale_min_at(d["x"].numpy(), d["weight"].numpy(), d["bias"].numpy(), pix, 2.0)
+    assert_close(got[pix[:, 0], 0, pix[:, 1], pix[:, 2]], ref, what=f"near-2GiB {layout}")
+
+
 def test_workload_tiny_full():
     wl = WORKLOADS["tiny_min_tanh2"]
     d = make_inputs(wl)
