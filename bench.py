@@ -11,7 +11,8 @@ epilogue (608.8 GFLOP per step).  Prints ONE JSON line on stdout.
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize() on both sides (wall clock -> ms_per_step).  HIP
 events recorded on the launch stream around the same K launches give the
-per-launch kernel duration used for the roofline figure.  The other four
+per-launch kernel duration used for the roofline figure (also given as a
+fraction of the MFMA-loop probe's throughput measured in the same run).  The other four
 workloads are timed before the headline one (unless --no-others), which
 also brings the GPU clocks to steady state first.  Every timing other than
 the headline's warms up for at least WARM_S seconds of its own work: after
@@ -187,6 +188,21 @@ def time_op(torch, op, steps, warmup, min_warm_s=0.0):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
+def mfma_loop(torch, x3, dev):
+    """The practical fp32 matrix-core ceiling on this GPU: the library's
+    MFMA-loop probe (one 4-wave workgroup per CU, 8 independent
+    32x32x2 fp32 MFMA chains per wavefront, no memory traffic), timed like
+    the workloads; its outputs have a closed form (256 * iters)."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    n_out, iters = cus * 256, 8192
+    out = torch.empty(n_out, device=dev)
+    _, ms = time_op(torch, lambda: x3.probe_mfma(out, iters), 10, 3, WARM_S)
+    tf = x3.probe_mfma_flop(n_out, iters) / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 2), "frac_peak": round(tf / PEAK_FP32_MFMA_TFLOPS, 4),
+            "exact": bool((out == 256.0 * iters).all().item()), "kernel_ms": round(ms, 4),
+            "workgroups": cus, "iters": iters}
 
 
 def gpu_inputs(torch, wl, dev, seed=0, cpu_inputs=None):
@@ -396,6 +412,9 @@ def main():
     tflops = flops / (ms_wall * 1e-3) / 1e12
     achieved = flops / (ms_kernel * 1e-3) / 1e12
 
+    # The practical MFMA ceiling, right after the headline timing.
+    loop = mfma_loop(torch, x3, dev)
+
     traffic = load_traffic(args.workload)
     roof = {
         "bound": "mfma",
@@ -405,6 +424,7 @@ def main():
         "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
         "traffic": traffic["bytes_per_launch"] if traffic else None,
         "kernel_ms": round(ms_kernel, 4),
+        "frac_of_mfma_loop": round(achieved / loop["tflops"], 4),
         "algorithmic_flop_per_launch": flops,
         "algorithmic_bytes_per_launch": algorithmic_bytes(wl),
     }
@@ -509,6 +529,7 @@ def main():
         "unfused_ablation": abl,
         "nhwc_workloads": nhwc,
         "copy_reference": copy_ref,
+        "mfma_loop": loop,
         "host": {"cpu": platform.processor() or platform.machine(), "cpu_count": os.cpu_count(),
                  "device": torch.cuda.get_device_name(0)},
     }

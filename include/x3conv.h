@@ -272,6 +272,17 @@ const char* x3_last_error(void);
 /* Library version string. */
 const char* x3_version(void);
 
+/* Measurement aid, not part of the method: the fp32 matrix-core throughput
+ * of a pure MFMA loop, the practical ceiling against which the conv
+ * kernels' fractions of the published peak can also be read.  Launches
+ * n_out / 256 workgroups of 256 threads; every wavefront runs `iters` rounds
+ * of 8 independent v_mfma_f32_32x32x2_f32 chains on constant operands (no
+ * memory traffic) and every thread writes one float to out[n_out] (device
+ * memory, caller-owned), which is exactly 256 * iters.  Matrix FLOP per
+ * call: (n_out / 64) * iters * 8 * 4096.  n_out a positive multiple of 256
+ * and 1 <= iters <= 65535, else X3_EINVAL; asynchronous on `stream`. */
+x3_status x3_probe_mfma_f32(float* out, int n_out, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

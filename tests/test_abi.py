@@ -318,3 +318,19 @@ def test_noalloc_gn_validation(lib):
     assert lib.x3_conv3x3_gn_workspace_bytes(1024, 8, 128, 128, 64, 16, 4) > x3.NOALLOC_SCRATCH_BYTES
     assert call(B=1024, H=128, W=128) == EWS
     assert b"static scratch" in lib.x3_last_error()
+
+
+def test_probe_mfma_validation():
+    """The MFMA-loop probe rejects a null output, an output length that is
+    not a positive multiple of 256, and an iteration count outside
+    1..65535, before launching anything."""
+    lib = x3.load_library()
+    f = lib.x3_probe_mfma_f32
+    s = P(0)
+    assert f(None, 256, 10, s) == EINVAL
+    for n in (0, -256, 100, 257):
+        assert f(O, n, 10, s) == EINVAL
+    for it in (0, -1, 65536):
+        assert f(O, 256, it, s) == EINVAL
+    assert b"iters" in lib.x3_last_error()
+    assert x3.probe_mfma_flop(256, 10) == 4 * 10 * 8 * 4096

@@ -24,6 +24,7 @@ __all__ = [
     "conv3x3_bias", "epi_min_tanh2", "epi_scale_min", "epi_mul_lrelu_gelu",
     "epi_mul_lrelu_gelu_tanh", "epi_gn_scale_pool_clamp",
     "library_path", "version", "X3Error", "load_library", "EXPORTED_SYMBOLS",
+    "probe_mfma", "probe_mfma_flop",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "x3_epi_min_tanh2_f32", "x3_epi_scale_min_f32", "x3_epi_mul_lrelu_gelu_f32",
     "x3_epi_mul_lrelu_gelu_tanh_f32", "x3_epi_gn_workspace_bytes",
     "x3_epi_gn_scale_pool_clamp_f32",
-    "x3_status_str", "x3_last_error", "x3_version",
+    "x3_status_str", "x3_last_error", "x3_version", "x3_probe_mfma_f32",
 )
 
 STATUS_NAMES = {0: "X3_OK", 1: "X3_EINVAL", 2: "X3_ESHAPE", 3: "X3_EUNSUPPORTED",
@@ -108,6 +109,7 @@ def load_library():
     lib.x3_last_error.restype = ctypes.c_char_p
     lib.x3_version.argtypes = []
     lib.x3_version.restype = ctypes.c_char_p
+    lib.x3_probe_mfma_f32.argtypes = [vp, i, i, vp]
     _lib = lib
     return lib
 
@@ -388,4 +390,21 @@ def epi_gn_scale_pool_clamp(y, gamma, beta, scale, groups=16, eps=1e-5, pool_k=4
     _check("x3_epi_gn_scale_pool_clamp_f32", lib.x3_epi_gn_scale_pool_clamp_f32(
         _ptr(y), _ptr(g), _ptr(be), _ptr(s), int(groups), float(eps), k, float(lo),
         float(hi), _ptr(out), _ptr(workspace), ws_bytes, B, C, H, W, _stream(y.device)))
+    return out
+
+
+def probe_mfma_flop(n_out: int, iters: int) -> int:
+    """Matrix FLOP of one x3_probe_mfma_f32 call."""
+    return (n_out // 64) * iters * 8 * 2 * 32 * 32 * 2
+
+
+def probe_mfma(out: torch.Tensor, iters: int) -> torch.Tensor:
+    """The fp32 MFMA-loop probe (a measurement aid, not part of the method):
+    len(out)/256 workgroups, every wavefront `iters` rounds of 8 independent
+    32x32x2 fp32 MFMAs on constant operands; every element of out becomes
+    exactly 256 * iters.  Asynchronous on the current stream."""
+    lib = load_library()
+    out = _tensor(out, "out", 1)
+    _check("x3_probe_mfma_f32",
+           lib.x3_probe_mfma_f32(_ptr(out), out.numel(), int(iters), _stream(out.device)))
     return out

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["x3conv.hip", "epi_min_tanh2.hip", "epi_mul_lrelu_gelu.hip",
            "epi_mul_lrelu_gelu_tanh.hip", "epi_scale_min.hip", "epi_gn_pool.hip",
-           "epi_split.hip", "epi_nhwc.hip", "epi_gn_poolk.hip", "epi_gn_poolk_nhwc.hip"]
+           "epi_split.hip", "epi_nhwc.hip", "epi_gn_poolk.hip", "epi_gn_poolk_nhwc.hip",
+           "probe.hip"]
 LIB = os.path.join(PKG, "libx3conv.so")
 ARCH = "gfx950"
 

@@ -227,6 +227,8 @@ x3_status launch_gn_finalize(const x3::GnFinArgs& f, int nblocks,
 // GroupNorm finalize, and the GroupNorm partial slots of the NHWC tiles.
 x3_status launch_nhwc(const x3::ConvArgs& a, int epi, hipStream_t st);
 x3_status launch_gn_finalize_nhwc(x3::GnFinArgs f, int B, hipStream_t st);
+// The fp32 MFMA-loop probe (probe.hip), `blocks` workgroups of 256 threads.
+x3_status launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
 int gn_pps_nhwc(int Ho, int Wo, int Cin, int Cout);
 
 // GroupNorm partial slots per (sample, group or channel) for this shape: one

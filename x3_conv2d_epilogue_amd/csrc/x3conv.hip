@@ -682,3 +682,12 @@ X3_API const char* x3_status_str(x3_status s) {
 X3_API const char* x3_last_error(void) { return g_err; }
 
 X3_API const char* x3_version(void) { return "x3conv 0.1.0 (gfx950)"; }
+
+X3_API x3_status x3_probe_mfma_f32(float* out, int n_out, int iters, void* stream) {
+  if (!out) return x3i::fail(X3_EINVAL, "out is NULL");
+  if (n_out <= 0 || n_out % 256 != 0)
+    return x3i::fail(X3_EINVAL, "n_out must be a positive multiple of 256 (got %d)", n_out);
+  if (iters < 1 || iters > 65535)
+    return x3i::fail(X3_EINVAL, "iters must be in 1..65535 (got %d)", iters);
+  return x3i::launch_mfma_probe(out, n_out / 256, iters, (hipStream_t)stream);
+}
