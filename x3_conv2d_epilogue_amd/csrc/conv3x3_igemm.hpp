@@ -281,12 +281,13 @@ __device__ __forceinline__ float swz_xor16(float v) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
 }
-// The value lane 0 holds (for lanes 0..31) or lane 32 holds (lanes 32..63).
-__device__ __forceinline__ float half_lane0(float v, int h) {
-  const int bits = __builtin_bit_cast(int, v);
-  const int lo = __builtin_amdgcn_readlane(bits, 0);
-  const int hi = __builtin_amdgcn_readlane(bits, 32);
-  return __builtin_bit_cast(float, h ? hi : lo);
+// The value lane 0 holds (for lanes 0..31) or lane 32 holds (lanes 32..63):
+// a bit-mode swizzle with all masks zero reads lane 0 of each 32-lane half
+// (one LDS-pipe instruction instead of two readlanes and a select).  Every
+// lane must be active, as everywhere in the epilogues.
+__device__ __forceinline__ float half_lane0(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x0000));
 }
 // Sum over the 32 lanes of a half-wave, returned to every lane of it.
 __device__ __forceinline__ float sum32(float v) {
@@ -944,7 +945,7 @@ __global__ void __launch_bounds__(G::NTHR)
       // first pixel
       f32x8 kv;
 #pragma unroll
-      for (int gi = 0; gi < 8; ++gi) kv[gi] = half_lane0(acc[gi >> 2][0][4 * (gi & 3)], h);
+      for (int gi = 0; gi < 8; ++gi) kv[gi] = half_lane0(acc[gi >> 2][0][4 * (gi & 3)]);
       // in-lane sums over the lane's pixels: sv[2gi] = S1, sv[2gi+1] = S2
       f32x16 sv;
       auto lane_sums = [&](auto masked) X3_INLINE {
@@ -1053,7 +1054,7 @@ __global__ void __launch_bounds__(G::NTHR)
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const int i = 8 * hs + k;
-            const float K = half_lane0(acc[mt][0][i], h);
+            const float K = half_lane0(acc[mt][0][i]);
             kv[k] = K;
             float u1 = 0.0f, u2 = 0.0f;
 #pragma unroll
@@ -1319,7 +1320,19 @@ __global__ void __launch_bounds__(G::NTHR)
     const int cb = pos.cb, chunk = pos.chunk;
     const int t = vb + pos.tl * G_;
 
-    if (chunk == 0) {
+    // One resident K chunk (RC == 1; the host guarantees one chunk and one
+    // channel block): every item starts a tile, and the first k-step's
+    // MFMAs take the bias as their C operand (no accumulator moves).
+    constexpr bool BIAS_C = G::RC == 1;
+    f32x16 binit[BIAS_C ? G::MT : 1];
+    if constexpr (BIAS_C) {
+      const X3_LDS float* sb = (const X3_LDS float*)s_bias;
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          binit[mt][i] = sb[mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3)];
+    } else if (chunk == 0) {
       // accumulators start at the bias
       const X3_LDS float* sb = (const X3_LDS float*)s_bias + cb * G::COUT;
 #pragma unroll
@@ -1428,7 +1441,7 @@ __global__ void __launch_bounds__(G::NTHR)
           acc[mt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
               A4 ? a4[(s / 4) & 1][mt][s % 4] : av[s & 1][mt],
               G::NH4 ? b4[(s / 4) & 1][G::NH4 ? j : 0][s % 4] : bv[s & 1][j],
-              acc[mt][j], 0, 0, 0);
+              (BIAS_C && s == 0) ? binit[BIAS_C ? mt : 0] : acc[mt][j], 0, 0, 0);
       // Issue order inside the step: each MFMA (64 cycles in the matrix
       // core) is followed by a slice of this wave's other work -- LDS
       // fragment reads, staging address arithmetic, one staging load -- so
