@@ -228,6 +228,21 @@ def test_gn_pool_samples_of_different_scales():
                  what="per-sample scales")
 
 
+@pytest.mark.parametrize("B", [20, 128])
+def test_gn_pool_row_offsets_and_sample_scales(B):
+    """GroupNorm statistics of samples whose top rows carry a large offset
+    (a row tile's values then lie far from those of the tiles below it),
+    scaled by different powers of ten, with more row tiles than
+    workgroups (B=20: 640 row tiles on 512 workgroups)."""
+    d = random_case("gn_scale_pool_clamp", B, 8, 130, 130, 64, seed=611)
+    d["x"][:, :, :40, :] += 50.0
+    d["x"][0::3] *= 1e-2
+    d["x"][1::3] *= 30.0
+    kw = dict(lo=-1e3, hi=1e3)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw), run_oracle("gn_scale_pool_clamp", d, **kw),
+                 what=f"shift reuse B={B}")
+
+
 def test_edge_minimal_spatial():
     """H = W = 3: a single output pixel per sample."""
     d = random_case("min_tanh2", 3, 7, 3, 3, 64, seed=700)
