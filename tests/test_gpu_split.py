@@ -108,11 +108,13 @@ def test_epi_mul_lrelu_gelu_flat_blocks(shape):
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 7])
 @pytest.mark.parametrize("cg", [(16, 4), (12, 3), (8, 8), (6, 1)])
-@pytest.mark.parametrize("hw", [(23, 29), (22, 30), (23, 30), (13, 260)])
+@pytest.mark.parametrize("hw", [(23, 29), (22, 30), (23, 30), (13, 260), (20, 32), (26, 126),
+                                (18, 128)])
 def test_epi_gn_any_pool(k, cg, hw):
     """Odd and even row lengths (even rows with 4x4 windows take the
-    one-kernel group form with 8-byte row spans), planes of a multiple of
-    4 floats or not, one and several 128-column spans, remainder rows and
+    one-kernel group form with 8-byte row spans; rows of 4m and 4m+2
+    floats, the latter the benchmark's 126), planes of a multiple of 4
+    floats or not, one and several 128-column spans, remainder rows and
     columns outside the last window."""
     C, groups = cg
     shape = (2, C) + hw

@@ -549,50 +549,64 @@ gn_group_k4w2_kernel(const GnGroupArgs a) {
     const int c = c0 + pl;
     const float* yb = a.y + ((int64_t)n * a.C + c) * P;
     float* eb = s_ext + pl * PP;
+    // (uniform per wavefront) the plane keeps its windows' maximum or
+    // minimum: the direction the GroupNorm-affine-scale map preserves
     const bool keep_max = (a.gamma[c] >= 0.0f) == (a.scale[c] >= 0.0f);
     const float Kf = yb[0];
     float s1 = 0.0f, s2 = 0.0f;
     constexpr int UNR = 3;  // units in flight (4 would exceed 64 registers)
-    for (int u0 = 0; u0 < nunits; u0 += UNR) {
-      float2 v[UNR][4];
-      // unit u: row band py, this lane's first column x (recomputed after
-      // the loads rather than kept: registers bound the occupancy here)
-      auto unit = [&](int u, int& py, int& x) X3_EPI_INLINE {
-        py = u / nsx;
-        x = (u - py * nsx) * 128 + 2 * lane;
-        return u < nunits && x < a.W;  // (W even: x + 1 < W too)
-      };
+    // unit u: row band py, this lane's first column x (recomputed after
+    // the loads rather than kept: registers bound the occupancy here)
+    auto unit = [&](int u, int& py, int& x) X3_EPI_INLINE {
+      py = u / nsx;
+      x = (u - py * nsx) * 128 + 2 * lane;
+      return u < nunits && x < a.W;  // (W even: x + 1 < W too)
+    };
+    // One compile-time direction per loop (one extremum chain per element
+    // instead of a maximum and a minimum), and a lane's unit sums dropped
+    // after the fact when the unit or its columns are not in the plane
+    // (two selects per unit instead of one per element).
+    auto stream = [&](auto maxc) X3_EPI_INLINE {
+      constexpr bool MX = decltype(maxc)::value;
+      for (int u0 = 0; u0 < nunits; u0 += UNR) {
+        float2 v[UNR][4];
 #pragma unroll
-      for (int q = 0; q < UNR; ++q) {
-        int py, x;
-        const bool ok = unit(u0 + q, py, x);
-        // (a unit past the end, or a lane past the row, reads the plane's
-        // first two columns instead: no load leaves the plane)
-        const float* src = yb + (ok ? py * 4 * a.W + x : 0);
+        for (int q = 0; q < UNR; ++q) {
+          int py, x;
+          const bool ok = unit(u0 + q, py, x);
+          // (a unit past the end, or a lane past the row, reads the plane's
+          // first two columns instead: no load leaves the plane)
+          const float* src = yb + (ok ? py * 4 * a.W + x : 0);
 #pragma unroll
-        for (int dy = 0; dy < 4; ++dy)
-          v[q][dy] = *reinterpret_cast<const float2*>(src + dy * a.W);
-      }
-#pragma unroll
-      for (int q = 0; q < UNR; ++q) {
-        int py, x;
-        const bool ok = unit(u0 + q, py, x);
-        float mx = -__builtin_inff(), mn = __builtin_inff();
-#pragma unroll
-        for (int dy = 0; dy < 4; ++dy) {
-          const float d0 = ok ? v[q][dy].x - Kf : 0.0f;
-          const float d1 = ok ? v[q][dy].y - Kf : 0.0f;
-          s1 += d0 + d1;
-          s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
-          mx = fmaxf(mx, fmaxf(v[q][dy].x, v[q][dy].y));
-          mn = fminf(mn, fminf(v[q][dy].x, v[q][dy].y));
+          for (int dy = 0; dy < 4; ++dy)
+            v[q][dy] = *reinterpret_cast<const float2*>(src + dy * a.W);
         }
-        // the 2 lanes of a window are an even/odd pair
-        mx = fmaxf(mx, quad_swap<0xB1>(mx));
-        mn = fminf(mn, quad_swap<0xB1>(mn));
-        if (ok && (lane & 1) == 0 && x + 3 < cw) eb[py * a.Pw + x / 4] = keep_max ? mx : mn;
+#pragma unroll
+        for (int q = 0; q < UNR; ++q) {
+          int py, x;
+          const bool ok = unit(u0 + q, py, x);
+          float u1 = 0.0f, u2 = 0.0f;
+          float m = MX ? -__builtin_inff() : __builtin_inff();
+#pragma unroll
+          for (int dy = 0; dy < 4; ++dy) {
+            const float d0 = v[q][dy].x - Kf, d1 = v[q][dy].y - Kf;
+            u1 += d0 + d1;
+            u2 = fmaf(d0, d0, fmaf(d1, d1, u2));
+            m = MX ? fmaxf(m, fmaxf(v[q][dy].x, v[q][dy].y))
+                   : fminf(m, fminf(v[q][dy].x, v[q][dy].y));
+          }
+          s1 += ok ? u1 : 0.0f;
+          s2 += ok ? u2 : 0.0f;
+          // the 2 lanes of a window are an even/odd pair
+          m = MX ? fmaxf(m, quad_swap<0xB1>(m)) : fminf(m, quad_swap<0xB1>(m));
+          if (ok && (lane & 1) == 0 && x + 3 < cw) eb[py * a.Pw + x / 4] = m;
+        }
       }
-    }
+    };
+    if (keep_max)
+      stream(std::true_type{});
+    else
+      stream(std::false_type{});
     // the rows below the last window, for the statistics (8-byte pairs)
     const int half = a.W / 2;
     const int rem = (a.H - rh) * half;
