@@ -190,6 +190,33 @@ def time_op(torch, op, steps, warmup, min_warm_s=0.0):
     return (t1 - t0) * 1e3 / steps, ev0.elapsed_time(ev1) / steps
 
 
+def graph_ms_per_call(torch, op, calls=20, replays=20):
+    """Per-call time of `op` replayed from a HIP graph of `calls` back-to-back
+    calls (no host launch work per call): for launch-bound workloads."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        op()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            op()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / (replays * calls)
+
+
 def mfma_loop(torch, x3, dev):
     """The practical fp32 matrix-core ceiling on this GPU: the library's
     MFMA-loop probe (one 4-wave workgroup per CU, 8 independent
@@ -402,6 +429,11 @@ def main():
                 "frac_fp32_mfma_peak": round(f2 / (mk * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
                 "steps": steps2,
             }
+            if w2.B * w2.Cout < 1024:
+                # launch-bound: the same call replayed from a HIP graph
+                gm = graph_ms_per_call(torch, op2)
+                others[name]["graph_ms_per_call"] = round(gm, 4)
+                others[name]["graph_tflops"] = round(f2 / (gm * 1e-3) / 1e12, 3)
             if args.cpu_budget > 0:
                 pending.append((others[name], w2, g2, o2, 1500))
             del g2, o2, ws2, op2
