@@ -132,6 +132,35 @@ def test_epi_gn_any_pool(k, cg, hw):
     assert_close(got, ref, what=f"k={k}")
 
 
+@pytest.mark.parametrize("hw", [(10, 14), (22, 30), (19, 128)])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_epi_gn_many_groups_unaligned_out(hw, offset):
+    """Groups of 4 planes of at most 128 columns, 2400 (sample, group)
+    workgroups: one window row per plane pair (10 x 14), an odd number of
+    window rows (22 x 30), a full 128-column row with 3 remainder rows
+    (19 x 128); out 16-byte aligned (16-byte stores) and, offset by one
+    float, not (4-byte stores).  Nothing is written outside out."""
+    B, C, groups = 1200, 8, 2
+    shape = (B, C) + hw
+    say(f"epi gn {shape} groups={groups} k=4 out offset={offset}")
+    y, x, w, b = identity_case(*shape, seed=700 + hw[0] + offset)
+    g = torch.Generator().manual_seed(70 + offset)
+    gamma = (1.0 + 0.2 * torch.randn(C, generator=g)).float()
+    gamma[::3] *= -1.0
+    beta = (0.1 * torch.randn(C, generator=g)).float()
+    scale = (1.0 + 0.2 * torch.randn(C, generator=g)).float()
+    ph, pw = hw[0] // 4, hw[1] // 4
+    buf = torch.full((B * C * ph * pw + 1,), float("nan"), device=DEV)
+    out = buf[offset:offset + B * C * ph * pw].view(B, C, ph, pw)
+    x3.epi_gn_scale_pool_clamp(y.to(DEV), gamma.to(DEV), beta.to(DEV), scale.to(DEV),
+                               groups, 1e-5, 4, -2.0, 2.0, out=out)
+    ref = oracle.gn_scale_pool_clamp(x, w, b, gamma.numpy(), beta.numpy(), scale.numpy(),
+                                     groups, 1e-5, 4, -2.0, 2.0)
+    assert_close(out, ref, what=f"{hw} offset {offset}")
+    rest = buf[B * C * ph * pw:] if offset == 0 else buf[:1]
+    assert torch.isnan(rest).all(), "a store left the output"
+
+
 @pytest.mark.parametrize("groups", [1, 4])
 def test_epi_gn_pooled_block_beyond_lds(groups):
     """4x4 windows on even rows: a group whose pooled block fits the LDS

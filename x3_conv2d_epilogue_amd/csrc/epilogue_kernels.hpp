@@ -522,10 +522,23 @@ struct GnGroupArgs {
   float eps, lo, hi;
 };
 
-__device__ __forceinline__ double wave_sum64_d(double v) {
-#pragma unroll
-  for (int mask = 1; mask < 64; mask <<= 1) v += __shfl_xor(v, mask, 64);
-  return v;
+// Sum over the 64 lanes of a wavefront, the same value in every lane, in
+// a fixed order: DPP steps inside each row of 16 lanes (the two quad swaps,
+// then rotations of the row by 4 and by 8 lanes) leave every lane with its
+// row's sum, and the four row sums are read out and added.  (Lane
+// permutations on the vector unit: a few cycles each, where a shuffle
+// through the LDS crossbar waits for a round trip.)
+__device__ __forceinline__ float wave_sum64_f(float v) {
+  v += quad_swap<0xB1>(v);
+  v += quad_swap<0x4E>(v);
+  v += quad_swap<0x124>(v);  // row rotate right by 4
+  v += quad_swap<0x128>(v);  // row rotate right by 8
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // (a template only so that every translation unit may include it)
@@ -533,7 +546,8 @@ template <int K4 = 4>
 __global__ void __launch_bounds__(kEpiThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 gn_group_k4w2_kernel(const GnGroupArgs a) {
   constexpr int NT = kEpiThreads, NWV = NT / 64;
-  extern __shared__ float s_ext[];  // [cpg][Ph*Pw] parked extrema
+  // [cpg][Ph*Pw] parked extrema (16-byte aligned: read as float4 below)
+  extern __shared__ __attribute__((aligned(16))) float s_ext[];
   __shared__ double s_ps[kGnGroupMaxCpg], s_pm[kGnGroupMaxCpg];
   __shared__ float s_A[kGnGroupMaxCpg], s_B[kGnGroupMaxCpg];
   __shared__ float s_mu;
@@ -541,6 +555,14 @@ gn_group_k4w2_kernel(const GnGroupArgs a) {
   const int n = blockIdx.x / groups, g = blockIdx.x - n * groups;
   const int c0 = g * a.cpg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // thread p < cpg computes plane p's output map after the statistics:
+  // its parameters are requested now, while the group streams in
+  float gam = 0.0f, sca = 0.0f, bet = 0.0f;
+  if (tid < a.cpg) {
+    gam = a.gamma[c0 + tid];
+    sca = a.scale[c0 + tid];
+    bet = a.beta[c0 + tid];
+  }
   const int P = a.H * a.W, PP = a.Ph * a.Pw;
   const int cw = a.Pw * 4, rh = a.Ph * 4;
   const int nsx = (a.W + 127) / 128;  // 128-column steps per row band
@@ -625,8 +647,11 @@ gn_group_k4w2_kernel(const GnGroupArgs a) {
         s2 = fmaf(d0, d0, fmaf(d1, d1, s2));
       }
     }
-    const double S1 = wave_sum64_d((double)s1);
-    const double S2 = wave_sum64_d((double)s2);
+    // (the lane sums about Kf carry no large common offset, so their float
+    // sum over the wavefront is good to a few ulp; the plane's (sum, M2)
+    // are then formed in double)
+    const double S1 = (double)wave_sum64_f(s1);
+    const double S2 = (double)wave_sum64_f(s2);
     if (lane == 0) {
       const double np = (double)P;
       s_ps[pl] = np * (double)Kf + S1;        // the plane's sum
@@ -634,33 +659,52 @@ gn_group_k4w2_kernel(const GnGroupArgs a) {
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    // Chan: M2 = sum_p [M2_p + P (mean_p - mean)^2], all planes of P elements
+  if (tid < a.cpg) {
+    // Chan: M2 = sum_p [M2_p + P (mean_p - mean)^2], all planes of P
+    // elements; each of these threads forms the same sums in the same order
     const double np = (double)P, total = np * a.cpg;
-    const bool has = lane < a.cpg;
-    const double mean = wave_sum64_d(has ? s_ps[lane] : 0.0) / total;
-    double t = 0.0;
-    if (has) {
-      const double dm = s_ps[lane] / np - mean;
-      t = s_pm[lane] + np * dm * dm;
+    double sum = 0.0;
+    for (int p = 0; p < a.cpg; ++p) sum += s_ps[p];
+    const double mean = sum / total;
+    double m2 = 0.0;
+    for (int p = 0; p < a.cpg; ++p) {
+      const double dm = s_ps[p] / np - mean;
+      m2 += s_pm[p] + np * dm * dm;
     }
-    const double m2 = wave_sum64_d(t);
     const float rstd = (float)(1.0 / sqrt(m2 / total + (double)a.eps));
-    if (has) {
-      const int c = c0 + lane;
-      s_A[lane] = rstd * a.gamma[c] * a.scale[c];
-      s_B[lane] = a.beta[c] * a.scale[c];
-    }
-    if (lane == 0) s_mu = (float)mean;
+    s_A[tid] = rstd * gam * sca;
+    s_B[tid] = bet * sca;
+    if (tid == 0) s_mu = (float)mean;
   }
   __syncthreads();
   const float mu = s_mu;
+  // the group's output planes are one contiguous block of cpg * PP floats
   float* ob = a.out + ((int64_t)n * a.C + c0) * PP;
-  for (int pl = 0; pl < a.cpg; ++pl) {
-    const float A = s_A[pl], Bc = s_B[pl];
-    for (int k = tid; k < PP; k += NT)
-      ob[pl * PP + k] = fminf(fmaxf(fmaf(s_ext[pl * PP + k] - mu, A, Bc), a.lo), a.hi);
+  const int tot = a.cpg * PP;
+  if ((((uintptr_t)ob & 15u) | (uint32_t)(tot & 3)) == 0) {
+    // 16-byte stores; an element's plane is idx / PP, taken as
+    // (idx + 0.5) * (1 / PP) (exact: the block fits kGnGroupMaxLdsBytes,
+    // so tot <= 12288 and the product's rounding stays far below its
+    // distance 0.5 / PP to an integer)
+    const float rpp = 1.0f / (float)PP;
+    for (int k = tid; 4 * k < tot; k += NT) {
+      const float4 e = *reinterpret_cast<const float4*>(s_ext + 4 * k);
+      float r[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int pl = (int)(((float)(4 * k + q) + 0.5f) * rpp);
+        r[q] = fminf(fmaxf(fmaf(r[q] - mu, s_A[pl], s_B[pl]), a.lo), a.hi);
+      }
+      *reinterpret_cast<float4*>(ob + 4 * k) = make_float4(r[0], r[1], r[2], r[3]);
+    }
+  } else {
+    for (int pl = 0; pl < a.cpg; ++pl) {
+      const float A = s_A[pl], Bc = s_B[pl];
+      for (int k = tid; k < PP; k += NT)
+        ob[pl * PP + k] = fminf(fmaxf(fmaf(s_ext[pl * PP + k] - mu, A, Bc), a.lo), a.hi);
+    }
   }
 }
+
 
 }  // namespace x3
