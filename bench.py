@@ -251,6 +251,18 @@ def gpu_inputs(torch, wl, dev, seed=0, cpu_inputs=None):
     return d
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo where there is one)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(wl, cpu_in, gpu_out, budget_s):
     """Time the oracle on a contiguous batch slice [0, b) of the workload,
     b chosen so the run takes about `budget_s` seconds; compare the GPU
@@ -382,6 +394,10 @@ def main():
 
     log(f"generating {wl.about} (seed 0, CPU)")
     cpu_in = make_inputs(wl, seed=0)
+    # (sum, sum of magnitudes) of each input, in double: identifies the draw
+    sums = {k: [round(float(v.sum(dtype=torch.float64)), 6),
+                round(float(torch.linalg.vector_norm(v, 1, dtype=torch.float64)), 6)]
+            for k, v in cpu_in.items()}
     g = gpu_inputs(torch, wl, dev, cpu_inputs=cpu_in)
     out = torch.empty(out_shape(wl), device=dev)
     ws = None
@@ -553,7 +569,7 @@ def main():
         "data": "synthetic (seeded: x~N(0,1), w,b~U(+-1/sqrt(Cin*9)))",
         "config": {"workload": wl.about, "x_shape": [wl.B, wl.Cin, wl.H, wl.W],
                    "cout": wl.Cout, "out_shape": list(out_shape(wl)), "seed": 0,
-                   "flop_per_step": flops},
+                   "flop_per_step": flops, "input_checksums": sums},
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,
@@ -562,9 +578,11 @@ def main():
         "nhwc_workloads": nhwc,
         "copy_reference": copy_ref,
         "mfma_loop": loop,
-        "host": {"cpu": platform.processor() or platform.machine(), "cpu_count": os.cpu_count(),
+        "host": {"cpu": cpu_model(), "cpu_count": os.cpu_count(),
                  "device": torch.cuda.get_device_name(0)},
     }
+    if cpu:
+        cpu["gpu_over_cpu"] = round(tflops / cpu["value"], 1)
     print(json.dumps(line), flush=True)
 
 
