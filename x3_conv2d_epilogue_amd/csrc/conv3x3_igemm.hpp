@@ -1522,12 +1522,42 @@ struct GnFinArgs {
   double count;      // elements per group: cpg * Ho * Wo
 };
 
-// Sum of a double over the workgroup (wave shuffles, then LDS); every
+// A DPP lane permutation of a double (each 32-bit half moved by one DPP
+// move; the controls used stay inside a row of 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF,
+                                                             0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL,
+                                                             0xF, 0xF, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// Sum over the 64 lanes of a wavefront in double, the same value in every
+// lane, in a fixed order: DPP steps inside each row of 16 lanes (the two
+// quad swaps, then rotations of the row by 4 and by 8 lanes) leave each
+// row's sum in its first lane, and the four row sums are read out and
+// added.  (Vector-unit lane moves of a few cycles each, where a shuffle
+// through the LDS crossbar waits for a round trip per step.)
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_d<DPP_QUAD_XOR1>(v);
+  v += dpp_d<DPP_QUAD_XOR2>(v);
+  v += dpp_d<DPP_ROW_ROR4>(v);
+  v += dpp_d<DPP_ROW_ROR8>(v);
+  return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+
+// Sum of a double over the workgroup (wavefront sums, then LDS); every
 // thread gets the total.  `red` holds one slot per wavefront.
 template <int NT>
 __device__ __forceinline__ double block_sum(double v, double* red) {
-#pragma unroll
-  for (int mask = 1; mask < 64; mask <<= 1) v += __shfl_xor(v, mask, 64);
+  v = wave_sum_d(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   double t = 0.0;
@@ -1674,12 +1704,6 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
 //      = sum_k (M2_k + s_k^2 / n_k) - (sum s_k)^2 / N,
 // the same sum as the pairwise (Chan) combination, reordered so that each
 // partial is read once.
-template <int NT>
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int mask = 1; mask < 64; mask <<= 1) v += __shfl_xor(v, mask, 64);
-  return v;
-}
 
 constexpr int kFinNhwcThreads = 1024;
 constexpr int kFinNhwcPerThread = 8;  // float4 (or floats) per thread
@@ -1750,8 +1774,8 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
 
   // group g's mean and 1/sigma from the wavefront's sums
   auto stats = [&](double sum, double sq, float& mu, float& rstd) {
-    sum = wave_sum_d<NT>(sum);
-    sq = wave_sum_d<NT>(sq);
+    sum = wave_sum_d(sum);
+    sq = wave_sum_d(sq);
     const double mean = sum / a.count;
     const double m2 = fmax(sq - sum * mean, 0.0);
     mu = (float)mean;
