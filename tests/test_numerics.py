@@ -129,3 +129,39 @@ def test_folded_gelu_catches_a_wrong_constant():
     r = q * np.exp2(-z * z)
     bad = z * np.where(z >= 0, 1.1774100225154747 - r, r)
     assert np.abs(bad - ref).max() > 1e-3
+
+
+def tanh_e2_f32(x):
+    """float32 emulation of the kernels' tanh: sign(x) (1 - e) / (1 + e),
+    e = 2^(-2|x| log2 e)."""
+    x = np.asarray(x, dtype=np.float32)
+    e = np.exp2(np.abs(x) * np.float32(-2.8853900817779268)).astype(np.float32)
+    return np.copysign((np.float32(1.0) - e) / (np.float32(1.0) + e), x).astype(np.float32)
+
+
+def test_tanh_e2_matches_tanh():
+    xs = np.linspace(-20.0, 20.0, 400001)
+    got = tanh_e2_f32(xs).astype(np.float64)
+    ref = np.tanh(xs)
+    assert np.max(np.abs(got - ref)) < 1e-6
+    # tanh(tanh(x)), as the channel-min epilogue applies it
+    got2 = tanh_e2_f32(tanh_e2_f32(xs)).astype(np.float64)
+    assert np.max(np.abs(got2 - np.tanh(np.tanh(xs)))) < 1e-6
+    # the special values
+    assert tanh_e2_f32(np.float32(0.0)) == 0.0
+    assert np.signbit(tanh_e2_f32(np.float32(-0.0)))
+    assert tanh_e2_f32(np.float32(np.inf)) == 1.0 and tanh_e2_f32(np.float32(-np.inf)) == -1.0
+    assert np.isnan(tanh_e2_f32(np.float32(np.nan)))
+    # odd, and monotone on a fine grid around 0
+    assert np.array_equal(tanh_e2_f32(-xs), -tanh_e2_f32(xs))
+    small = np.linspace(-1e-3, 1e-3, 20001)
+    assert np.all(np.diff(tanh_e2_f32(small).astype(np.float64)) >= 0.0)
+
+
+def test_tanh_e2_catches_a_wrong_constant():
+    """The pin above fails for a plausible slip: exp instead of exp2 with the
+    same constant."""
+    x = np.linspace(-4.0, 4.0, 10001)
+    e = np.exp(np.abs(x) * -2.8853900817779268)
+    wrong = np.copysign((1.0 - e) / (1.0 + e), x)
+    assert np.max(np.abs(wrong - np.tanh(x))) > 1e-2

@@ -803,7 +803,7 @@ __global__ void __launch_bounds__(G::NTHR)
       }
       auto finish = [&](float v) X3_INLINE {
         if constexpr (EPI == EPI_MIN_TANH2)
-          return tanhf(tanhf(v));
+          return tanh_e2(tanh_e2(v));
         else
           return a.s0 * v;
       };

@@ -51,7 +51,7 @@ struct ChanArgs {
 template <int MODE>
 __device__ __forceinline__ float chan_finish(float m, float scale) {
   if constexpr (MODE == CHAN_MIN_TANH2)
-    return tanhf(tanhf(m));
+    return tanh_e2(tanh_e2(m));
   else
     return scale * m;
 }
