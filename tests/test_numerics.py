@@ -54,9 +54,10 @@ def mul_lrelu_gelu_folded_f32(y, m, slope):
     """float32 emulation of the fused epilogue (b) as the kernels evaluate
     it: multiplier pre-scaled by kGeluIn = sqrt(log2(e)/2), A&S 7.1.26 with
     p' = p / sqrt(log2 e), coefficients scaled by c = 1 / (2 kGeluIn),
-    exp(-x^2) as 2^(-z^2), and 1 + erf picked by the LeakyReLU compare.
-    The reciprocal and exp2 are correctly rounded here; the hardware forms
-    are within 1 ulp of these."""
+    exp(-x^2) as 2^(-z^2), and 1 + erf picked by the LeakyReLU compare as
+    |base - q e| with base 1/kGeluIn or 0 (one fused rounding).  The
+    reciprocal and exp2 are correctly rounded here; the hardware forms are
+    within 1 ulp of these."""
     f = np.float32
     k_in = f(0.8493218002880191)
     c = f(0.5887050112577373)
@@ -71,9 +72,8 @@ def mul_lrelu_gelu_folded_f32(y, m, slope):
         q = _fma32(q, t, f(a) * c)
     q = (q * t).astype(np.float32)
     e = np.exp2(-(z * z).astype(np.float32)).astype(np.float32)
-    r = (q * e).astype(np.float32)
-    return (z * np.where(pos, (f(1.1774100225154747) - r).astype(np.float32), r)).astype(
-        np.float32)
+    base = np.where(pos, f(1.1774100225154747), f(0.0)).astype(np.float32)
+    return (z * np.abs(_fma32(-q, e, base))).astype(np.float32)
 
 
 def test_folded_gelu_constants_derive_from_the_published_ones():

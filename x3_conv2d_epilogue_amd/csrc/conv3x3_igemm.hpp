@@ -881,36 +881,52 @@ __global__ void __launch_bounds__(G::NTHR)
           }
         return;
       }
-      // NCHW: each store's byte offset is the channel's plane offset plus
-      // the pixel's, one add per store.  A dropped pixel's part is the drop
-      // bit alone, so the add cannot carry out of bit 31 (a channel's
-      // plane offset, padded channels included, is below 2 GiB).
-      uint32_t pixb[G::NW];
+      if constexpr (G::NHWC) {
 #pragma unroll
-      for (int j = 0; j < G::NW; ++j) pixb[j] = drop[j] ? drop[j] : pix_off[j] << 2;
-      // (the per-lane part of the channel's plane offset once; the rest is
-      // a constant times HoWo, a scalar product)
-      const uint32_t co_lane = (uint32_t)(co0 + 4 * h) * (uint32_t)HoWo;
+        for (int mt = 0; mt < G::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int co = co0 + 4 * h + mt * 32 + 8 * (i >> 2) + (i & 3);
+            const float mv = s_par[co];
+            const uint32_t co_off = (uint32_t)co | ((uint32_t)(co >= a.Cout) << 31);
+#pragma unroll
+            for (int j = 0; j < G::NW; ++j) {
+              // (OR, not add: nothing can clear the drop bits)
+              const uint32_t off =
+                  ((co_off + pix_off[j]) << 2) | drop[j] | (co_off & 0x80000000u);
+              __builtin_amdgcn_raw_buffer_store_b32(
+                  __builtin_bit_cast(uint32_t, op(acc[mt][j][i], mv)), o_rsrc, off, 0, 0);
+            }
+          }
+        return;
+      }
+      // NCHW: each store goes through a buffer resource based at the plane
+      // of lane half 0's channel cb (scalar: built per channel, with the
+      // records up to the end of the sample's block), so its offset is the
+      // lane's part alone -- lane half h's 4 channels further, plus the
+      // pixel -- computed once per tile: no vector instruction per store.
+      // A dropped pixel has bit 31 set, past every record count; a padded
+      // channel lies at or past its resource's end (lane half 1 at
+      // 4 * HoWo floats on, below 2 GiB since the padded channels' planes
+      // are), and a channel block wholly past Cout gets no records.
+      uint32_t voff[G::NW];
+#pragma unroll
+      for (int j = 0; j < G::NW; ++j)
+        voff[j] = drop[j] ? drop[j] : ((uint32_t)(4 * h) * (uint32_t)HoWo + pix_off[j]) << 2;
+      float* const ob = a.out + (size_t)n * a.Cout * HoWo;
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int cu = mt * 32 + 8 * (i >> 2) + (i & 3);
-          const int co = co0 + 4 * h + cu;
-          const float mv = s_par[co];
-          const uint32_t co_off =
-              G::NHWC ? (uint32_t)co | ((uint32_t)(co >= a.Cout) << 31)
-                      : co_lane + (uint32_t)cu * (uint32_t)HoWo;
+          const int cb = co0 + mt * 32 + 8 * (i >> 2) + (i & 3);
+          const int left = a.Cout - cb;  // channels from cb to the block's end
+          const __amdgpu_buffer_rsrc_t c_rsrc = make_rsrc(
+              ob + (size_t)cb * HoWo, left > 0 ? (uint32_t)left * (uint32_t)HoWo * 4u : 0u);
+          const float mv = s_par[cb + 4 * h];
 #pragma unroll
-          for (int j = 0; j < G::NW; ++j) {
-            const float y = op(acc[mt][j][i], mv);
-            // (NHWC: OR, not add: nothing can clear the drop bits)
-            const uint32_t off =
-                G::NHWC ? ((co_off + pix_off[j]) << 2) | drop[j] | (co_off & 0x80000000u)
-                        : (co_off << 2) + pixb[j];
+          for (int j = 0; j < G::NW; ++j)
             __builtin_amdgcn_raw_buffer_store_b32(
-                __builtin_bit_cast(uint32_t, y), o_rsrc, off, 0, 0);
-          }
+                __builtin_bit_cast(uint32_t, op(acc[mt][j][i], mv)), c_rsrc, voff[j], 0, 0);
         }
     } else {  // the GroupNorm epilogues: wave tiles of 4 rows
       static_assert(G::NW == 4, "GroupNorm epilogues need 4-row wave tiles");

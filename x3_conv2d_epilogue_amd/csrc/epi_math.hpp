@@ -30,7 +30,7 @@ __device__ __forceinline__ float lrelu(float v, float slope) {
 // coefficients scaled by 1 / (2 kGeluIn) (r = q' e):
 //   GELU(v) = z (1 / kGeluIn - r) for x >= 0,  z r for x < 0.
 // x >= 0 exactly when y * mk >= 0 or the slope is negative (neg_slope
-// set): then LeakyReLU maps both signs to z >= 0.  About 15 plain vector
+// set): then LeakyReLU maps both signs to z >= 0.  About 14 plain vector
 // operations and 2 transcendentals (one reciprocal, one exp2) per element,
 // against 19 and 2 for the formula evaluated as written.
 constexpr float kGeluIn = 0.8493218002880191f;  // sqrt(log2(e) / 2)
@@ -48,8 +48,11 @@ __device__ __forceinline__ float mul_lrelu_gelu_erf(float y, float mk, float slo
   q = fmaf(q, t, -0.284496736f * c);
   q = fmaf(q, t, 0.254829592f * c);
   q *= t;
-  const float r = q * __builtin_amdgcn_exp2f(-(z * z));
-  return z * (pos ? 1.1774100225154747f - r : r);  // 1 / kGeluIn
+  // with r = q e: |base - r| is 1/kGeluIn - r for x >= 0 (base 1/kGeluIn,
+  // r <= 1/(2 kGeluIn)) and r otherwise (base 0), one fused rounding
+  // either way
+  const float base = pos ? 1.1774100225154747f : 0.0f;  // 1 / kGeluIn
+  return z * fabsf(fmaf(-q, __builtin_amdgcn_exp2f(-(z * z)), base));
 }
 
 // tanh(x) = sign(x) (1 - e) / (1 + e), e = exp(-2|x|) = 2^(-2|x| log2 e):
