@@ -151,12 +151,16 @@ struct Geo {
   //    [XROWS][XCOLS][CCP], CCP = CC + 2.  With a pitch of 2 mod 4 dwords
   //    per pixel, the 32 pixels x 2 adjacent channels of a B-fragment read
   //    (lane half h reads channel 2cp + h) fall in 64 distinct banks.
-  //  * NH4, 16-byte staging (Cin % 4 == 0): two regions, channels 0-3 and
-  //    4-7 of the chunk, each [XROWS][XCOLS][4], so a 16-byte piece is one
-  //    pixel's 4 channels.  K order: k-step s takes tap s/4, and lane half
+  //  * NH4, 16-byte staging (Cin % 4 == 0): pixel-major, [XROWS][XCOLS][2]
+  //    slots of 4 channels; slot s of the pixel in column col holds channels
+  //    4(s ^ b3) .. 4(s ^ b3) + 3 of the chunk, b3 = bit 3 of col.  Two
+  //    adjacent lanes stage one pixel's 32 contiguous bytes, so a load
+  //    instruction touches 32 lines of x where separate channel-half
+  //    regions touched 64.  K order: k-step s takes tap s/4, and lane half
   //    h channel 4h + s%4, so a lane's B values of the 4 k-steps of a tap
-  //    are one ds_read_b128; 16 consecutive pixels at a 4-dword pitch cover
-  //    all 64 banks.
+  //    are one ds_read_b128 (slot h ^ b3); 16 consecutive columns at an
+  //    8-dword pitch cover all 64 banks, as columns 8 apart use opposite
+  //    slots.
   static constexpr bool NHWC = NHWC_;
   static constexpr bool NH4 = NHWC_ && X4_;
   static constexpr int CCP = CC + 2;
@@ -180,7 +184,7 @@ struct Geo {
   //    adjacent channels), odd weight pitch WP = KC + 1 (conflict-free
   //    4-byte reads).
   static constexpr bool KO = X4 && !NHWC;
-  static constexpr int RSZ = (XROWS * XCOLS * 4 + 255) / 256 * 256;  // NH4 region
+  static constexpr int PXS = XROWS * XCOLS * 8;  // NH4: dwords of the pixel slots
   static constexpr int CS0 = XROWS * XP;
   static constexpr int CS =
       KO ? CS0 + ((8 - (CS0 % 16)) + 16) % 16
@@ -188,7 +192,7 @@ struct Geo {
   static constexpr int KC = 9 * CC;       // K per chunk
   static constexpr int XBLK = X4 ? 256 : 64;
   static constexpr int XBUF =             // input dwords per stage
-      NH4    ? 2 * RSZ
+      NH4    ? (PXS + 255) / 256 * 256
       : NHWC ? (XROWS * XCOLS * CCP + 63) / 64 * 64
              : (CC * CS + XBLK - 1) / XBLK * XBLK;
   // weight-row pitch: 16-byte staged rows (KO and NH4) as described for KO
@@ -353,8 +357,6 @@ __global__ void __launch_bounds__(G::NTHR)
   const uint32_t x_sample = (uint32_t)a.Cin * a.H * a.W;  // floats
   constexpr bool PRE = G::X4;  // precomputed staging offsets (see below)
   const uint32_t w_total = (uint32_t)a.Cout * a.Cin * 9u;  // floats
-  // a buffer of no records: every load through it returns 0
-  const __amdgpu_buffer_rsrc_t x_null = make_rsrc(a.x, 0u);
 
   // ---- staging of one (tile, chunk) item ------------------------------------
   // The stage is filled in blocks, one direct-to-LDS load per block and
@@ -369,8 +371,8 @@ __global__ void __launch_bounds__(G::NTHR)
   // that reach only conv outputs outside the image, which are neither
   // stored nor counted) or lie past its end and read as 0.  Input channels
   // past Cin read as 0 too: in NCHW they start past the end of the sample;
-  // in NHWC (Cin % 8 == 4: the upper half of a last chunk) their blocks
-  // load through a buffer of no records.  Weight columns past the chunk's
+  // in NHWC (Cin % 8 == 4: the upper half of a last chunk) their pieces
+  // take offsets with the drop bit (xoffh).  Weight columns past the chunk's
   // K are masked.  The other configurations (4 times as many blocks, too
   // many registers to keep) compute masked offsets per item: rows past H,
   // input channels past Cin and weight columns past the chunk's K read as
@@ -476,20 +478,25 @@ __global__ void __launch_bounds__(G::NTHR)
   constexpr int NBWP = (NBWTP + G::NWAVE - 1) / G::NWAVE;  // per wave
   constexpr int NBWK = PW ? NBWP : G::NBW;  // weight blocks per wave
   uint32_t woff[PRE ? NBWK : 1], wkk[PRE && !PW ? G::NBW : 1];
-  constexpr int RBLK = G::RSZ / 256;  // NH4: blocks per channel-half region
+  // NH4: the same offsets with the pieces of the upper channel half
+  // dropped, for a last chunk of 4 channels (Cin % 8 == 4)
+  uint32_t xoffh[G::NH4 ? G::NBI : 1];
   if constexpr (G::NH4) {
 #pragma unroll
     for (int i = 0; i < G::NBI; ++i) {
       int blk = wave + i * G::NWAVE;
       blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
-      // lane l moves pixel pc's 4 channels of the block's half; pieces
-      // past the tile's pixels (region padding) are not loaded
-      const int hr = blk >= RBLK;
-      const uint32_t pc = (uint32_t)((blk - hr * RBLK) * 64 + lane);
+      // lane l moves slot sl of pixel pc: channels 4*hc .. 4*hc + 3, hc =
+      // sl ^ (bit 3 of the pixel's column); pieces past the tile's pixels
+      // (stage padding) are not loaded
+      const uint32_t P = (uint32_t)(blk * 64 + lane);
+      const uint32_t pc = P >> 1;
       const uint32_t row = pc / G::XCOLS;
       const uint32_t col = pc - row * G::XCOLS;
-      xoff[i] = (((row * (uint32_t)a.W + col) * (uint32_t)a.Cin + 4u * hr) << 2) |
+      const uint32_t hc = (P & 1u) ^ ((col >> 3) & 1u);
+      xoff[i] = (((row * (uint32_t)a.W + col) * (uint32_t)a.Cin + 4u * hc) << 2) |
                 ((uint32_t)(pc >= (uint32_t)(G::XROWS * G::XCOLS)) << 31);
+      xoffh[i] = xoff[i] | (hc << 31);
     }
   } else if constexpr (PRE) {
 #pragma unroll
@@ -554,9 +561,9 @@ __global__ void __launch_bounds__(G::NTHR)
     if (i < G::NBI && G::NH4) {
       int blk = wave + i * G::NWAVE;
       blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
-      // (uniform) the upper channel half of a last chunk with 4 channels
-      const bool none = blk >= RBLK && l.ci_lim <= 4;
-      lds_load_x4(none ? x_null : l.xr, (X3_LDS void*)(sbase + blk * 256), xoff[i]);
+      // (uniform) a last chunk with 4 channels: its upper half reads 0
+      lds_load_x4(l.xr, (X3_LDS void*)(sbase + blk * 256),
+                  l.ci_lim <= 4 ? xoffh[i] : xoff[i]);
     } else if (i < G::NBI && G::NHWC) {
       int blk = wave + zz + i * G::NWAVE;
       blk = blk < G::NBX - 1 ? blk : G::NBX - 1;
@@ -1361,8 +1368,15 @@ __global__ void __launch_bounds__(G::NTHR)
         }
     }
 
+    // NH4: the lane's pixel for tap column kw, in the slot that holds its
+    // half's channels (the slot order swaps every 8 columns)
+    const X3_LDS float* xsk[3];
+#pragma unroll
+    for (int kw = 0; kw < 3; ++kw)
+      xsk[kw] = cur + (wm.row0 * G::XCOLS + wm.strip * 32 + l32 + kw) * 8 +
+                4 * (h ^ (((l32 + kw) >> 3) & 1));
     const X3_LDS float* xs =
-        G::NH4    ? cur + h * G::RSZ + (wm.row0 * G::XCOLS + wm.strip * 32 + l32) * 4
+        G::NH4    ? xsk[0]
         : G::NHWC ? cur + (wm.row0 * G::XCOLS + wm.strip * 32 + l32) * G::CCP + h
         : G::KO   ? cur + h * (G::CC / 2) * G::CS + wm.row0 * G::XP +
                         wm.strip * 32 + l32
@@ -1387,8 +1401,7 @@ __global__ void __launch_bounds__(G::NTHR)
       const int kh = tap / 3, kw = tap % 3;
 #pragma unroll
       for (int j = 0; j < (G::NH4 ? G::NW : 1); ++j)
-        Bq[j] = *reinterpret_cast<const X3_LDS f32x4*>(
-            xs + ((j + kh) * G::XCOLS + kw) * 4);
+        Bq[j] = *reinterpret_cast<const X3_LDS f32x4*>(xsk[kw] + (j + kh) * G::XCOLS * 8);
     };
     auto load_a4 = [&](int g, f32x4 (&A)[A4 ? G::MT : 1]) X3_INLINE {
 #pragma unroll
