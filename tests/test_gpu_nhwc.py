@@ -124,6 +124,7 @@ def test_nhwc_gn_pool(shape, cg):
     ((1, 8, 200, 130), 64, 16),   # 200 partials per group: the finalize's looped merge
     ((2, 8, 34, 34), 30, 10),     # 30 channels: the finalize's 4-byte accesses
     ((1, 16, 12, 40), 128, 128),  # 128 groups of one channel
+    ((1, 8, 130, 130), 36, 9),    # 36 channels: a thread's float4 walk across channels
 ])
 def test_nhwc_gn_pool_finalize_paths(case):
     (B, Cin, H, W), Cout, groups = case

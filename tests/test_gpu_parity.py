@@ -188,6 +188,19 @@ def test_gn_pool_random(shape, lohi):
                  what=f"{shape}/{lohi}")
 
 
+@pytest.mark.parametrize("H", [130, 134])
+def test_gn_pool_finalize_block_sizes(H):
+    """Pooled group blocks at and just past what one finalize workgroup
+    holds in registers: 4 channels x 32 x 32 = 1024 float4 (H = 130) and
+    4 x 33 x 33 (H = 134, the looped form)."""
+    say(f"gn_pool finalize H={H}")
+    d = random_case("gn_scale_pool_clamp", 1, 8, H, H, 64, seed=650 + H)
+    d["gamma"][::3] *= -1.0
+    kw = dict(lo=-50.0, hi=50.0)
+    assert_close(run_op("gn_scale_pool_clamp", d, **kw), run_oracle("gn_scale_pool_clamp", d, **kw),
+                 what=f"H={H}")
+
+
 def test_gn_pool_negative_gamma_and_scale():
     d = random_case("gn_scale_pool_clamp", 2, 8, 30, 46, 64, seed=600)
     d["gamma"][::3] *= -1.0

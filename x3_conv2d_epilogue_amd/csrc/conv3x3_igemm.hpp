@@ -1694,6 +1694,38 @@ __global__ void __launch_bounds__(NT) gn_finalize_kernel(const GnFinArgs a) {
                    (e) < p1 ? B0 : ((e) < p2 ? B1 : ((e) < p3 ? B2 : B3))), \
               lo),                                                          \
         hi)
+  if constexpr (VEC) {
+    constexpr int PT = 4;
+    if (nvec <= PT * NT) {
+      // (uniform) at most PT float4 per thread: the thread's others are
+      // requested together now, after the merge (before it they would
+      // queue ahead of the partials that the merge waits for); an element
+      // past the block gets bit 31 in its offset and reads as zero
+      const __amdgpu_buffer_rsrc_t orr = make_rsrc(o, (uint32_t)nvec * 16u);
+      float4 v[PT];
+      v[0] = first;
+#pragma unroll
+      for (int r = 1; r < PT; ++r) {
+        const uint32_t k = (uint32_t)(tid + r * NT);
+        v[r] = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(
+                        orr, (k << 4) | ((uint32_t)(k >= (uint32_t)nvec) << 31), 0, 0));
+      }
+#pragma unroll
+      for (int r = 0; r < PT; ++r) {
+        const int k = tid + r * NT;
+        if (k >= nvec) break;
+        const int e = 4 * k;
+        float4 w;
+        w.x = X3_GN_OUT(v[r].x, e);
+        w.y = X3_GN_OUT(v[r].y, e + 1);
+        w.z = X3_GN_OUT(v[r].z, e + 2);
+        w.w = X3_GN_OUT(v[r].w, e + 3);
+        reinterpret_cast<float4*>(o)[k] = w;
+      }
+      return;
+    }
+  }
   for (int k = tid; k < nvec; k += NT) {
     if constexpr (VEC) {
       const float4 v =
@@ -1739,7 +1771,9 @@ constexpr int kFinNhwcPerThread = 8;  // float4 (or floats) per thread
 
 template <int NT, bool VEC>
 __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a) {
-  __shared__ float s_mu[kMaxCout], s_A[kMaxCout], s_B[kMaxCout];
+  __shared__ __attribute__((aligned(16))) float s_mu[kMaxCout];
+  __shared__ __attribute__((aligned(16))) float s_A[kMaxCout];
+  __shared__ __attribute__((aligned(16))) float s_B[kMaxCout];
   constexpr int NWV = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = blockIdx.x / a.nchunk, chunk = blockIdx.x - n * a.nchunk;
@@ -1849,19 +1883,42 @@ __global__ void __launch_bounds__(NT) gn_finalize_nhwc_kernel(const GnFinArgs a)
     }
   }
   __syncthreads();
+  if constexpr (VEC) {
+    // a float4 holds 4 consecutive channels c..c+3 (C % 4 == 0, so c is a
+    // multiple of 4 and their constants are one 16-byte LDS read each); a
+    // thread's next float4 lies 4*NT floats on, step channels further
+    // (mod C): with C dividing 4*NT (C = 64, 128, ...) the channels stay
+    // and the constants are read once
+    const int step = (4 * NT) % a.C;
+    int c = (4 * (beg + tid)) % a.C;
+    float4 mu, A, Bc;
+    auto fetch = [&] {
+      mu = *reinterpret_cast<const float4*>(&s_mu[c]);
+      A = *reinterpret_cast<const float4*>(&s_A[c]);
+      Bc = *reinterpret_cast<const float4*>(&s_B[c]);
+    };
+    fetch();
 #pragma unroll
-  for (int r = 0; r < kFinNhwcPerThread; ++r) {
-    const int k = beg + tid + r * NT;
-    if (k >= end) continue;
-    if constexpr (VEC) {
-      const int c = (4 * k) % a.C;  // 4 consecutive channels (C % 4 == 0)
+    for (int r = 0; r < kFinNhwcPerThread; ++r) {
+      if (r > 0 && step != 0) {
+        c += step;
+        c -= c >= a.C ? a.C : 0;
+        fetch();
+      }
+      const int k = beg + tid + r * NT;
+      if (k >= end) continue;
       float4 v = v4[r];
-      v.x = fminf(fmaxf(fmaf(v.x - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
-      v.y = fminf(fmaxf(fmaf(v.y - s_mu[c + 1], s_A[c + 1], s_B[c + 1]), a.lo), a.hi);
-      v.z = fminf(fmaxf(fmaf(v.z - s_mu[c + 2], s_A[c + 2], s_B[c + 2]), a.lo), a.hi);
-      v.w = fminf(fmaxf(fmaf(v.w - s_mu[c + 3], s_A[c + 3], s_B[c + 3]), a.lo), a.hi);
+      v.x = fminf(fmaxf(fmaf(v.x - mu.x, A.x, Bc.x), a.lo), a.hi);
+      v.y = fminf(fmaxf(fmaf(v.y - mu.y, A.y, Bc.y), a.lo), a.hi);
+      v.z = fminf(fmaxf(fmaf(v.z - mu.z, A.z, Bc.z), a.lo), a.hi);
+      v.w = fminf(fmaxf(fmaf(v.w - mu.w, A.w, Bc.w), a.lo), a.hi);
       reinterpret_cast<float4*>(o)[k] = v;
-    } else {
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kFinNhwcPerThread; ++r) {
+      const int k = beg + tid + r * NT;
+      if (k >= end) continue;
       const int c = k % a.C;
       o[k] = fminf(fmaxf(fmaf(v1[r] - s_mu[c], s_A[c], s_B[c]), a.lo), a.hi);
     }
