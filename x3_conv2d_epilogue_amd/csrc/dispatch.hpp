@@ -164,10 +164,17 @@ x3_status dispatch_mt4_rw(const x3::ConvArgs& a, hipStream_t st) {
 }
 
 // The 16-byte configurations (NCHW, or NHWC with NH), resident weights
-// when they fit: all K chunks of the one channel block.
+// when they fit: all K chunks of the one channel block.  NHWC with staged
+// weights takes 64-channel blocks whenever the GroupNorm partial layout
+// does not fix the block: their weight rows are staged in the K walk's
+// order (conflict-free fragment reads) where 128-channel blocks keep the
+// stored order, and two 64-channel passes beat one 128-channel pass (the
+// 64 -> 128 channel-min on [64,64,256,256]: 4.14-4.16 against 4.21 ms).
 template <int EPI, bool NH>
 x3_status dispatch_x4(const x3::ConvArgs& a, hipStream_t st) {
   const int mt = channel_block_mt(a.Cout);
+  if (NH && !x3::gn_epilogue<EPI>() && a.Cin > 16)
+    return dispatch_mt2<EPI, true, NH>(a, st);
   if (a.Cin <= 16 && a.Cout <= 32 * mt)
     return mt == 4 ? dispatch_mt4_rw<EPI, NH>(a, st) : dispatch_mt2_rw<EPI, NH>(a, st);
   return mt == 4 ? dispatch_mt4<EPI, true, NH>(a, st) : dispatch_mt2<EPI, true, NH>(a, st);
