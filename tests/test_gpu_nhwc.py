@@ -52,7 +52,7 @@ SHAPES = [  # (B, Cin, H, W)
 
 
 @pytest.mark.parametrize("shape", SHAPES)
-@pytest.mark.parametrize("Cout", [40, 64, 128, 200])
+@pytest.mark.parametrize("Cout", [40, 64, 96, 128, 200])
 def test_nhwc_scale_min_integer_bit_exact(shape, Cout):
     B, Cin, H, W = shape
     say(f"nhwc scale_min int-exact {shape} Cout={Cout}")
